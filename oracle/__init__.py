@@ -1,0 +1,49 @@
+"""Float64 CPU oracle for paged single-query decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it.  It shares no code, header, table or helper with the
+HIP library; both sides receive the same raw input arrays from the seeded
+generators in ``workloads/`` and compute independently.
+
+What it computes, and the passage each function follows:
+
+* ``formats``   -- exact widening of stored K/V/q elements (fp32, fp16, bf16)
+  and the 256-entry OCP E4M3FN decode table written from the format's
+  sign/exponent/mantissa definition.  FP8 KV storage with a scale is named on
+  youngju.dev, "KVキャッシュとPagedAttention — 推論メモリのすべて", section
+  "KV量子化: FP8とINT8" (one byte per element; a scale is needed).
+* ``paging``    -- the physical pool ``[num_blocks][H_kv][B][d]``, the scatter
+  of new tokens through a slot mapping, the block copy used by copy-on-write,
+  and the gather of a sequence's logical K/V through its block table
+  (0h-n0.github.io, "論文解説: Efficient Memory Management for Large Language
+  Model Serving with PagedAttention", sections "PagedAttentionのメモリ管理"
+  and "Copy-on-Write（CoW）によるメモリ共有"; dihengye.cn, "PagedAttention",
+  section "Block Table 结构").
+* ``attention`` -- the plain definition softmax(q K^T * scale) V for one
+  query row over the gathered keys (0h-n0.github.io explainer, section
+  "Attention計算"), the block-by-block online-softmax recurrence of
+  auturnal.com, "メモリ予算内での言語モデルのサービング", equation (4), and
+  the log-sum-exp merge of per-partition partial states that the same
+  recurrence implies.
+* ``accounting`` -- KV bytes per token (equation (1) of the auturnal.com
+  review; youngju.dev section "KVキャッシュはなぜメモリを消費するのか"),
+  page-tail waste and its bound (equation (2)), the exact mean tail waste for
+  uniform lengths (equation (3)) and the reservation comparison of section 5.
+
+Every floating-point result is computed in float64.  Parity status of each
+function is listed in its docstring; all are pinned by ``tests/test_oracle*.py``
+against closed forms, printed worked examples, library routines or brute force.
+"""
+
+from . import accounting, attention, formats, paging  # noqa: F401
+from .attention import (  # noqa: F401
+    dense_attention,
+    lse_merge,
+    online_softmax_attention,
+    paged_decode,
+    paged_decode_row,
+    split_kv_attention,
+)
+from .formats import decode_elements, e4m3fn_table  # noqa: F401
+from .paging import copy_blocks, gather_sequence, reshape_and_cache  # noqa: F401

@@ -1,0 +1,190 @@
+"""Pins for the oracle's element formats and paging (CPU only).
+
+Each check ties the oracle to something other than itself: a library
+conversion routine, hand-decoded codes, the block-table examples the pages
+print (``tests/golden/block_tables.json``), or a contiguous round trip.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats, paging
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+
+
+def test_e4m3fn_table_matches_torch_exhaustively():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = formats.e4m3fn_table()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    finite = ~np.isnan(ref)
+    assert np.array_equal(ours[finite], ref[finite])
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+    (0x38, 1.0), (0x40, 2.0), (0x3C, 1.5), (0x7E, 448.0), (0xFE, -448.0), (0xB8, -1.0),
+])
+def test_e4m3fn_hand_decoded_codes(code, value):
+    assert formats.e4m3fn_table()[code] == value
+
+
+def test_e4m3fn_nan_codes_and_negative_zero():
+    t = formats.e4m3fn_table()
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert int(np.isnan(t).sum()) == 2
+    assert t[0x80] == 0.0 and np.signbit(t[0x80])
+
+
+def test_bf16_widening_matches_torch_exhaustively():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = formats.bf16_bits_to_f64(bits)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+def test_f16_widening_matches_torch_exhaustively():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    ours = formats.f16_bits_to_f64(bits)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+def test_bf16_known_patterns():
+    assert formats.bf16_bits_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert formats.bf16_bits_to_f64(np.array([0xC000], np.uint16))[0] == -2.0
+    assert formats.bf16_bits_to_f64(np.array([0x3F81], np.uint16))[0] == 1.0 + 2.0 ** -7
+
+
+# ----------------------------------------------------------------- paging
+
+
+def _tagged_pool(num_blocks, heads, block_size, dim):
+    """Pool whose element (b, h, r, c) encodes its own coordinates."""
+    b, h, r, c = np.meshgrid(np.arange(num_blocks), np.arange(heads), np.arange(block_size),
+                             np.arange(dim), indexing="ij")
+    return (b * 1_000_000 + h * 10_000 + r * 100 + c).astype(np.int64)
+
+
+@pytest.mark.parametrize("example", _golden("block_tables.json")["examples"], ids=lambda e: e["name"])
+def test_gather_follows_printed_block_tables(example):
+    B = example["block_size"]
+    pool = _tagged_pool(16, 2, B, 3)
+    rows = paging.gather_sequence(pool, example["table"], example["seq_len"], B)
+    assert rows.shape == (2, example["seq_len"], 3)
+    for t in range(example["seq_len"]):
+        want_block = example["table"][t // B]
+        assert rows[1, t, 2] == want_block * 1_000_000 + 1 * 10_000 + (t % B) * 100 + 2
+    if "tokens_per_block" in example:
+        counts = [min(B, example["seq_len"] - k * B) for k in range(len(example["table"]))]
+        assert counts == example["tokens_per_block"]
+    if "token_blocks" in example:
+        for first, last, phys in example["token_blocks"]:
+            assert rows[0, first, 0] // 1_000_000 == phys
+            assert rows[0, last, 0] // 1_000_000 == phys
+
+
+def _contiguous_case(rng, seq_lens, heads, dim, block_size, spare=5):
+    """Contiguous K/V per sequence, random physical tables, slot mapping."""
+    need = [-(-t // block_size) for t in seq_lens]
+    pool_size = sum(need) + spare
+    perm = rng.permutation(pool_size)
+    tables, start = [], 0
+    for n in need:
+        tables.append(perm[start:start + n])
+        start += n
+    keys = [rng.standard_normal((t, heads, dim)) for t in seq_lens]
+    values = [rng.standard_normal((t, heads, dim)) for t in seq_lens]
+    slots = [np.array([tab[t // block_size] * block_size + t % block_size for t in range(T)], np.int64)
+             for tab, T in zip(tables, seq_lens)]
+    return pool_size, tables, keys, values, slots
+
+
+@pytest.mark.parametrize("block_size", [1, 3, 16, 32])
+def test_scatter_then_gather_round_trips_bitwise(block_size):
+    rng = np.random.default_rng(11)
+    B = block_size
+    seq_lens = [1, B - 1 if B > 1 else 1, B, B + 1, 3 * B + 2, 100]
+    heads, dim = 3, 8
+    pool_size, tables, keys, values, slots = _contiguous_case(rng, seq_lens, heads, dim, B)
+    kc = np.full((pool_size, heads, B, dim), np.nan)
+    vc = np.full((pool_size, heads, B, dim), np.nan)
+    for k, v, s in zip(keys, values, slots):
+        paging.reshape_and_cache(kc, vc, k, v, s, B)
+    for i, T in enumerate(seq_lens):
+        gk = paging.gather_sequence(kc, tables[i], T, B)
+        gv = paging.gather_sequence(vc, tables[i], T, B)
+        assert np.array_equal(gk, keys[i].transpose(1, 0, 2))
+        assert np.array_equal(gv, values[i].transpose(1, 0, 2))
+
+
+def test_scatter_skips_negative_slots_and_touches_nothing_else():
+    kc = np.zeros((4, 2, 4, 3))
+    vc = np.zeros((4, 2, 4, 3))
+    key = np.ones((3, 2, 3))
+    value = 2 * np.ones((3, 2, 3))
+    paging.reshape_and_cache(kc, vc, key, value, np.array([5, -1, 14]), 4)
+    assert np.all(kc[1, :, 1] == 1) and np.all(vc[1, :, 1] == 2)
+    assert np.all(kc[3, :, 2] == 1) and np.all(vc[3, :, 2] == 2)
+    assert kc.sum() == 2 * 2 * 3 and vc.sum() == 2 * 2 * 2 * 3
+
+
+def test_copy_blocks_copies_whole_blocks_and_leaves_the_rest():
+    kc = _tagged_pool(8, 2, 4, 3).astype(np.float64)
+    vc = -kc
+    k0, v0 = kc.copy(), vc.copy()
+    paging.copy_blocks(kc, vc, np.array([[1, 6], [3, 7], [1, 5]]))
+    for s, d in [(1, 6), (3, 7), (1, 5)]:
+        assert np.array_equal(kc[d], k0[s]) and np.array_equal(vc[d], v0[s])
+    for b in [0, 1, 2, 3, 4]:
+        assert np.array_equal(kc[b], k0[b]) and np.array_equal(vc[b], v0[b])
+
+
+def test_copy_blocks_reads_contents_from_before_the_call():
+    kc = _tagged_pool(4, 1, 2, 1).astype(np.float64)
+    vc = kc.copy()
+    k0 = kc.copy()
+    # block 1 is both a destination and (later in the list) a source
+    paging.copy_blocks(kc, vc, np.array([[0, 1], [1, 2]]))
+    assert np.array_equal(kc[1], k0[0]) and np.array_equal(kc[2], k0[1])
+
+
+def test_copy_on_write_copy_preserves_logical_contents():
+    """A sequence remapped to a copied block reads the same logical rows."""
+    rng = np.random.default_rng(3)
+    B, heads, dim = 4, 2, 5
+    pool_size, tables, keys, values, slots = _contiguous_case(rng, [10], heads, dim, B, spare=3)
+    kc = np.zeros((pool_size, heads, B, dim))
+    vc = np.zeros((pool_size, heads, B, dim))
+    paging.reshape_and_cache(kc, vc, keys[0], values[0], slots[0], B)
+    used = set(int(x) for x in tables[0])
+    spare = [b for b in range(pool_size) if b not in used]
+    table = tables[0].copy()
+    paging.copy_blocks(kc, vc, np.array([[table[2], spare[0]]]))
+    table[2] = spare[0]
+    assert np.array_equal(paging.gather_sequence(kc, table, 10, B), keys[0].transpose(1, 0, 2))
+    assert np.array_equal(paging.gather_sequence(vc, table, 10, B), values[0].transpose(1, 0, 2))
+
+
+def test_package_exports():
+    for name in ["dense_attention", "paged_decode", "online_softmax_attention", "split_kv_attention",
+                 "lse_merge", "reshape_and_cache", "copy_blocks", "gather_sequence", "e4m3fn_table"]:
+        assert callable(getattr(oracle, name))

@@ -1,0 +1,214 @@
+/*
+ * pagedattn.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * The library implements the GPU side of PagedAttention: the KV cache is cut
+ * into fixed-size physical blocks of B tokens, and each sequence reaches its
+ * tokens through a block table that maps logical block k (tokens k*B ..
+ * k*B+B-1) to a physical block id (0h-n0.github.io, "論文解説: Efficient
+ * Memory Management for Large Language Model Serving with PagedAttention",
+ * section "PagedAttentionのメモリ管理"; dihengye.cn, "PagedAttention",
+ * section "核心思想").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *_cache, key, value, q, out, slot_mapping, block_pairs,
+ *   block_tables, seq_lens, k_scale, v_scale and workspace are DEVICE
+ *   pointers.  All other arguments are host scalars.
+ * - `stream` is a hipStream_t handle (NULL = the null stream).  Every call is
+ *   asynchronous on that stream, never synchronises and never reads device
+ *   memory on the host.
+ * - The library owns no memory and allocates none: the caller owns every
+ *   buffer, including the split-KV workspace of pa_decode.  It keeps no
+ *   global state; concurrent calls on different streams are independent as
+ *   long as their output buffers do not overlap.
+ * - Physical KV pool layout (one array for K, one for V):
+ *       cache[num_blocks][num_kv_heads][block_size][head_dim]
+ *   in the element format `kv_dtype`, contiguous, 16-byte aligned.  One
+ *   (block, kv head) tile of block_size*head_dim elements is contiguous.
+ * - Return value: PA_OK (0) or a negative pa_status.  Argument errors are
+ *   detected on the host before anything is launched; then nothing runs.
+ *   PA_ERR_LAUNCH reports a failed kernel launch.
+ * - Device contents are not validated on the host.  Kernels guard every
+ *   device-supplied index that would address memory: an out-of-range slot or
+ *   block pair is skipped, and a sequence whose length or block ids are out
+ *   of range gets a row of NaN in `out` instead of a memory access.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.  PA_DTYPE_FP8_E4M3 is the OCP 8-bit float E4M3FN (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN =
+ * 0x7F/0xFF, largest finite 448), stored one byte per element with a float32
+ * scale per kv head: value = decoded_code * scale.  FP8 KV storage with a
+ * scale is named on youngju.dev, "KVキャッシュとPagedAttention — 推論メモリの
+ * すべて", section "KV量子化: FP8とINT8". */
+typedef enum pa_dtype {
+    PA_DTYPE_F32 = 0,
+    PA_DTYPE_F16 = 1,
+    PA_DTYPE_BF16 = 2,
+    PA_DTYPE_FP8_E4M3 = 3
+} pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    PA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
+    PA_ERR_DTYPE = -3,       /* unknown dtype code or unsupported dtype combination */
+    PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, block_size, GQA group */
+    PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_size()   */
+    PA_ERR_LAUNCH = -6       /* the HIP runtime rejected a kernel launch           */
+} pa_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * pa_reshape_and_cache -- store the K and V rows of new tokens in their slots.
+ *
+ * Keeping each token's K and V once computed, for reuse by every later
+ * decode step, is what the KV cache is for (youngju.dev, same page, section
+ * "核心原理: KVキャッシュとは何か"); blocks are taken one at a time as a
+ * sequence grows (section "PagedAttention: OS仮想メモリ式の管理").
+ *
+ * For every token t < num_tokens with s = slot_mapping[t]:
+ *     k_cache[s / block_size][h][s % block_size][:] = key[t][h][:]
+ *     v_cache[s / block_size][h][s % block_size][:] = value[t][h][:]
+ * for all kv heads h.  The copy is bitwise (elements are moved as bytes).
+ *   key, value   [num_tokens][num_kv_heads][head_dim], kv_dtype, 16-B aligned
+ *   k_cache, v_cache   pool as described above, kv_dtype
+ *   slot_mapping [num_tokens] int64.  s < 0 means "skip this token".  A slot
+ *                at or beyond num_blocks*block_size is skipped as well.
+ *                Two tokens with the same slot in one call: which one lands
+ *                is unspecified.
+ *   head_dim     64 or 128;  block_size 16 or 32.
+ * num_tokens == 0 is a valid no-op.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, int kv_dtype,
+                         void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks for copy-on-write.
+ *
+ * When a sequence must write into a block whose reference count exceeds one,
+ * a new block is allocated, the shared block's contents are copied into it,
+ * the old block's count is decremented and the table entry remapped
+ * (0h-n0.github.io explainer, section "Copy-on-Write（CoW）によるメモリ共有").
+ * This call performs the copy step for a batch of such blocks; the host
+ * block manager does the rest.
+ *
+ * For every pair p < num_pairs with (src, dst) = (block_pairs[2p], block_pairs[2p+1]):
+ *     k_cache[dst][:][:][:] = k_cache[src][:][:][:]   (all kv heads, all rows)
+ *     v_cache[dst][:][:][:] = v_cache[src][:][:][:]
+ * bitwise.  Precondition: destinations are distinct and none is also a
+ * source in the same call (then every pair reads the contents from before
+ * the call).  Pairs with an id outside [0, num_blocks) are skipped.
+ *   block_pairs  [num_pairs][2] int64, device memory.
+ * num_pairs == 0 is a valid no-op.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int num_blocks, int kv_dtype,
+                   void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs.
+ *
+ * Holds one partial state (m, l, acc[head_dim]) in float32 per (sequence,
+ * query head, KV partition), with ceil(max_seq_len / partition_size)
+ * partitions per sequence.  Returns 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_seq_len,
+                                int partition_size);
+
+/*
+ * pa_decode -- single-query attention of every sequence over its paged K/V.
+ *
+ * For sequence i with T = seq_lens[i] cached tokens (the current token
+ * included) and query head h, with G = num_heads / num_kv_heads and kv head
+ * g = h / G (consecutive query heads share a kv head; youngju.dev, same
+ * page, section "GQAとMQA"):
+ *     K_i, V_i = rows 0..T-1 of the sequence, token t read from physical
+ *                block block_tables[i][t / block_size], row t % block_size,
+ *                kv head g (dequantised: code * k_scale[g] / * v_scale[g] for FP8)
+ *     out[i][h][:] = softmax(scale * K_i q[i][h]) V_i
+ * which is the attention of the current query against all cached tokens
+ * (0h-n0.github.io explainer, section "Attention計算").  T == 0 gives a row
+ * of zeros.
+ *
+ * Method: the tokens of a sequence are split into partitions of
+ * partition_size tokens (a multiple of block_size; partition p covers
+ * [p*P, min((p+1)P, T)), so no partition is empty).  One workgroup per
+ * (sequence, kv head, partition) walks the partition's blocks with the
+ * online-softmax recurrence of auturnal.com, "メモリ予算内での言語モデルのサー
+ * ビング", equation (4): m' = max(m, max_j s_j), l' = e^{m-m'} l +
+ * sum_j e^{s_j-m'}, and the value accumulator rescaled by the same factor,
+ * for all G query heads of the kv head at once.  A second kernel merges the
+ * partition states of each (sequence, query head) with the same rule in a
+ * fixed partition order.  Sequences with a single partition are finished by
+ * the first kernel.  Results are deterministic (bitwise identical between
+ * calls and independent of which physical blocks hold the data).
+ *
+ *   out          [num_seqs][num_heads][head_dim], out_dtype (F32, F16 or BF16)
+ *   q            [num_seqs][num_heads][head_dim], q_dtype
+ *   k_cache, v_cache   pool, kv_dtype
+ *   block_tables [num_seqs][max_blocks_per_seq] int32; entries at and beyond
+ *                ceil(seq_lens[i]/block_size) are never read
+ *   seq_lens     [num_seqs] int32, device; each must lie in [0, max_seq_len]
+ *                and need at most max_blocks_per_seq blocks
+ *   max_seq_len  host upper bound of seq_lens (sizes the grid and workspace)
+ *   num_blocks   number of physical blocks in the pool (bounds block ids)
+ *   scale        softmax scale, typically 1/sqrt(head_dim)
+ *   k_scale, v_scale   [num_kv_heads] float32, device; required for FP8 KV,
+ *                ignored (may be NULL) otherwise
+ *   partition_size     tokens per KV partition, a positive multiple of block_size
+ *   workspace    device scratch of at least pa_decode_workspace_size(num_seqs,
+ *                num_heads, head_dim, max_seq_len, partition_size) bytes,
+ *                256-byte aligned; its contents on entry do not matter
+ *
+ * Supported: head_dim 64 or 128; block_size 16 or 32; G in {1, 2, 4, 8};
+ * (kv_dtype, q_dtype) in {(F32, F32), (F16, F16), (BF16, BF16),
+ * (FP8_E4M3, BF16)}; out_dtype F32, F16 or BF16.  Accumulation is float32.
+ */
+int pa_decode(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+              const void* v_cache, int kv_dtype, const int32_t* block_tables,
+              int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+              float scale, const float* k_scale, const float* v_scale, int partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partition, pa_decode_reduce -- the two launches of pa_decode,
+ * exported separately so that a caller can time them individually.  Called
+ * in this order on one stream with identical arguments they are exactly
+ * pa_decode.  pa_decode_partition writes the workspace (and the rows of
+ * single-partition sequences); pa_decode_reduce reads it and writes the
+ * remaining rows.
+ */
+int pa_decode_partition(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                        const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                        int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                        int block_size, int num_blocks, float scale, const float* k_scale,
+                        const float* v_scale, int partition_size, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                     const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                     int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int num_blocks, float scale, const float* k_scale, const float* v_scale,
+                     int partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,117 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libpagedattn.so``
+(``include/pagedattn.h``): the functions below carry the C names and only
+marshal arguments (device pointers of torch tensors, sizes, dtype codes and
+the current HIP stream).  Every step of the computation runs in the HIP
+kernels; PyTorch is used for device memory and streams only.
+
+``BlockManager`` (``blocks.py``) is the host-side block allocator with
+reference counts and copy-on-write that produces block tables, slot mappings
+and copy pairs for these calls.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from .blocks import BlockManager, PoolExhausted  # noqa: F401
+
+PA_DTYPE_F32, PA_DTYPE_F16, PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": PA_DTYPE_F32, "f16": PA_DTYPE_F16, "bf16": PA_DTYPE_BF16,
+               "fp8_e4m3": PA_DTYPE_FP8_E4M3}
+_TORCH_CODES = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16,
+                torch.float8_e4m3fn: PA_DTYPE_FP8_E4M3, torch.uint8: PA_DTYPE_FP8_E4M3}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = _lib.load().pa_status_string(status).decode()
+        super().__init__(f"{call} failed: {msg} ({status})")
+
+
+def dtype_code(t: torch.Tensor, override=None) -> int:
+    """Element-format code of a tensor (``override`` may name it: 'bf16', ...)."""
+    if override is not None:
+        return DTYPE_CODES[override] if isinstance(override, str) else int(override)
+    try:
+        return _TORCH_CODES[t.dtype]
+    except KeyError:
+        raise ValueError(f"no element format for {t.dtype}; pass it explicitly") from None
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpagedattn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status, call):
+    if status != 0:
+        raise PagedAttnError(status, call)
+
+
+def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, kv_dtype=None, stream=None):
+    """Scatter ``key``/``value`` ``[T][H_kv][d]`` into the pools at ``slot_mapping``."""
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    _check(_lib.load().pa_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.numel()),
+        num_kv_heads, head_dim, block_size, num_blocks, dtype_code(k_cache, kv_dtype),
+        _stream(stream, k_cache.device)), "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, kv_dtype=None, stream=None):
+    """Copy whole blocks for each ``(src, dst)`` row of ``block_pairs`` (int64, device)."""
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    _check(_lib.load().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), int(block_pairs.numel() // 2), num_kv_heads, head_dim,
+        block_size, num_blocks, dtype_code(k_cache, kv_dtype), _stream(stream, k_cache.device)),
+        "pa_copy_blocks")
+
+
+def pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partition_size) -> int:
+    return int(_lib.load().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partition_size))
+
+
+def _decode_call(name, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
+                 partition_size, workspace, k_scale=None, v_scale=None, kv_dtype=None, q_dtype=None,
+                 out_dtype=None, stream=None):
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    num_seqs, num_heads, _ = q.shape
+    fn = getattr(_lib.load(), name)
+    _check(fn(_ptr(out), dtype_code(out, out_dtype), _ptr(q), dtype_code(q, q_dtype), _ptr(k_cache),
+              _ptr(v_cache), dtype_code(k_cache, kv_dtype), _ptr(block_tables), int(block_tables.shape[1]),
+              _ptr(seq_lens), int(max_seq_len), num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+              num_blocks, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace),
+              int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
+              _stream(stream, q.device)), name)
+
+
+def pa_decode(*args, **kw):
+    """``out[i][h] = softmax(scale * K_i q[i][h]) V_i`` over each sequence's paged K/V.
+
+    Arguments: ``out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len,
+    scale, partition_size, workspace`` and, for FP8 pools, ``k_scale`` and
+    ``v_scale``; see ``include/pagedattn.h``.
+    """
+    _decode_call("pa_decode", *args, **kw)
+
+
+def pa_decode_partition(*args, **kw):
+    """First launch of ``pa_decode`` (partition states into the workspace)."""
+    _decode_call("pa_decode_partition", *args, **kw)
+
+
+def pa_decode_reduce(*args, **kw):
+    """Second launch of ``pa_decode`` (merge of the partition states)."""
+    _decode_call("pa_decode_reduce", *args, **kw)

@@ -1,0 +1,49 @@
+"""ctypes loader for ``libpagedattn.so`` (the C ABI in ``include/pagedattn.h``).
+
+The library is built in-tree by ``paged_kv_cache_142_amd.build``; there is no
+fallback: if it is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
+
+# Names and signatures of every exported function (kept in the order of the
+# header).
+_c_int, _c_size, _c_float, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+_DECODE_ARGS = [_vp, _c_int, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
+                _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _c_int, _vp, _c_size, _vp]
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [_c_int]),
+    "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      _c_int, _vp]),
+    "pa_copy_blocks": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "pa_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pa_decode": (_c_int, _DECODE_ARGS),
+    "pa_decode_partition": (_c_int, _DECODE_ARGS),
+    "pa_decode_reduce": (_c_int, _DECODE_ARGS),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library once and attach the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_142_amd.build` "
+            "(the HIP library is required; there is no CPU path)")
+    lib = ctypes.CDLL(path)
+    for name, (restype, argtypes) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = restype
+        fn.argtypes = argtypes
+    _lib = lib
+    return lib

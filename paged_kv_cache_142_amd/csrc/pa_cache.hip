@@ -1,0 +1,118 @@
+// KV-cache maintenance kernels for gfx950: the slot scatter of new tokens
+// (pa_reshape_and_cache) and the whole-block copy used by copy-on-write
+// (pa_copy_blocks).  Both move stored elements as 16-byte granules, so they
+// are bitwise and independent of the element format.
+//
+// Pool layout: cache[num_blocks][num_kv_heads][block_size][head_dim]; one
+// token row of one head is head_dim * elem_bytes contiguous bytes (64..512,
+// always a multiple of 16).
+
+#include "pa_common.hpp"
+
+namespace pa {
+
+// One thread per 16-byte granule of the (token, K|V, head, granule) space.
+// The granule index runs fastest over the row, then heads, then K/V, then
+// tokens, so consecutive lanes read consecutive source bytes.
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                         u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+                         const int64_t* __restrict__ slot_mapping, int64_t total_granules,
+                         int granules_per_row, int num_kv_heads, int block_size,
+                         int64_t num_slots) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total_granules) return;
+    const int per_token = 2 * num_kv_heads * granules_per_row;
+    const int64_t t = idx / per_token;
+    const int rem = (int)(idx - t * per_token);
+    const int which = rem / (num_kv_heads * granules_per_row);  // 0 = K, 1 = V
+    const int hg = rem - which * num_kv_heads * granules_per_row;
+    const int h = hg / granules_per_row;
+    const int g = hg - h * granules_per_row;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t block = slot / block_size;
+    const int64_t row = slot - block * block_size;
+    const int64_t src = (t * num_kv_heads + h) * granules_per_row + g;
+    const int64_t dst = ((block * num_kv_heads + h) * block_size + row) * granules_per_row + g;
+    if (which == 0)
+        k_cache[dst] = key[src];
+    else
+        v_cache[dst] = value[src];
+}
+
+// grid.y = pair, grid.z = K|V; each thread copies one 16-byte granule of
+// the whole (all heads, all rows) block.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+                   const int64_t* __restrict__ block_pairs, int granules_per_block,
+                   int64_t num_blocks) {
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= granules_per_block) return;
+    const int64_t src = block_pairs[2 * (int64_t)blockIdx.y];
+    const int64_t dst = block_pairs[2 * (int64_t)blockIdx.y + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    u32x4* cache = blockIdx.z == 0 ? k_cache : v_cache;
+    cache[dst * granules_per_block + g] = cache[src * granules_per_block + g];
+}
+
+static bool valid_kv_dtype(int d) { return d >= PA_DTYPE_F32 && d <= PA_DTYPE_FP8_E4M3; }
+static bool supported_dim(int d) { return d == 64 || d == 128; }
+static bool supported_block(int b) { return b == 16 || b == 32; }
+
+}  // namespace pa
+
+extern "C" const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+        case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent size";
+        case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown or unsupported dtype combination";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or GQA group not built";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+        case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+        default: return "unknown pa_status";
+    }
+}
+
+extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping, int num_tokens,
+                                    int num_kv_heads, int head_dim, int block_size,
+                                    int num_blocks, int kv_dtype, void* stream) {
+    using namespace pa;
+    if (!valid_kv_dtype(kv_dtype)) return PA_ERR_DTYPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_SHAPE;
+    if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    const int granules_per_row = head_dim * dtype_bytes(kv_dtype) / 16;
+    const int64_t total = (int64_t)num_tokens * 2 * num_kv_heads * granules_per_row;
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0,
+                       (hipStream_t)stream, (const u32x4*)key, (const u32x4*)value,
+                       (u32x4*)k_cache, (u32x4*)v_cache, slot_mapping, total, granules_per_row,
+                       num_kv_heads, block_size, (int64_t)num_blocks * block_size);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                              int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, int kv_dtype, void* stream) {
+    using namespace pa;
+    if (!valid_kv_dtype(kv_dtype)) return PA_ERR_DTYPE;
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_SHAPE;
+    if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+    if (num_pairs > 65535) return PA_ERR_SHAPE;
+    const int64_t granules = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype) / 16;
+    if (granules > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const unsigned gx = (unsigned)((granules + 255) / 256);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0,
+                       (hipStream_t)stream, (u32x4*)k_cache, (u32x4*)v_cache, block_pairs,
+                       (int)granules, (int64_t)num_blocks);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}

@@ -1,0 +1,198 @@
+// pa_decode entry points: host-side validation, workspace layout, the
+// log-sum-exp reduce kernel, and dispatch to the partition kernels.
+
+#include <math.h>
+
+#include "pa_decode_kernel.hpp"
+
+namespace pa {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int num_partitions(int max_seq_len, int partition_size) {
+    return (max_seq_len + partition_size - 1) / partition_size;
+}
+
+// Workspace: m[N][H][P_max] | l[N][H][P_max] | acc[N][H][P_max][D], float32,
+// each array starting on a 256-byte boundary.
+static size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int max_parts) {
+    const size_t rows = (size_t)num_seqs * num_heads * max_parts;
+    return 2 * align256(rows * 4) + rows * head_dim * 4;
+}
+
+// Merge the partition states of one (sequence, query head); one thread per
+// output element.  Partitions are visited in index order, so the result is
+// deterministic.  Also writes the rows the partition kernel does not: empty
+// sequences (zeros) and invalid ones (NaN).
+template <int D>
+__global__ void __launch_bounds__(D) decode_reduce_kernel(const DecodeArgs a) {
+    const int seq = blockIdx.x / a.num_heads;
+    const int hq = blockIdx.x - seq * a.num_heads;
+    const int d = threadIdx.x;
+    const int T = a.seq_lens[seq];
+    const size_t row = (size_t)seq * a.num_heads + hq;
+    float o;
+    if (T < 0 || T > a.max_seq_len || (T + a.block_size - 1) / a.block_size > a.max_blocks_per_seq) {
+        o = __builtin_nanf("");
+    } else if (T == 0) {
+        o = 0.f;
+    } else {
+        const int n_parts = (T + a.partition_size - 1) / a.partition_size;
+        if (n_parts == 1) return;  // finished by the partition kernel
+        const size_t base = row * a.max_partitions;
+        float M = -INFINITY;
+        for (int p = 0; p < n_parts; ++p) M = fmaxf(M, a.part_m[base + p]);
+        float L = 0.f, A = 0.f;
+        for (int p = 0; p < n_parts; ++p) {
+            const float f = fast_exp2(a.part_m[base + p] - M);
+            L = fmaf(f, a.part_l[base + p], L);
+            A = fmaf(f, a.part_acc[(base + p) * D + d], A);
+        }
+        o = A / L;
+    }
+    store_out(a.out, a.out_dtype, row * D + d, o);
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Prepared {
+    DecodeArgs args;
+    int head_dim;
+    int group;
+    int kv_dtype;
+    int q_dtype;
+    bool nothing_to_do;
+};
+
+static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_dtype,
+                   const void* k_cache, const void* v_cache, int kv_dtype,
+                   const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+                   int max_seq_len, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                   int block_size, int num_blocks, float scale, const float* k_scale,
+                   const float* v_scale, int partition_size, void* workspace,
+                   size_t workspace_bytes) {
+    const bool combo_ok = (kv_dtype == PA_DTYPE_F32 && q_dtype == PA_DTYPE_F32) ||
+                          (kv_dtype == PA_DTYPE_F16 && q_dtype == PA_DTYPE_F16) ||
+                          (kv_dtype == PA_DTYPE_BF16 && q_dtype == PA_DTYPE_BF16) ||
+                          (kv_dtype == PA_DTYPE_FP8_E4M3 && q_dtype == PA_DTYPE_BF16);
+    if (!combo_ok) return PA_ERR_DTYPE;
+    if (out_dtype != PA_DTYPE_F32 && out_dtype != PA_DTYPE_F16 && out_dtype != PA_DTYPE_BF16)
+        return PA_ERR_DTYPE;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+        max_blocks_per_seq < 0 || num_blocks <= 0 || partition_size <= 0 || block_size <= 0 ||
+        head_dim <= 0)
+        return PA_ERR_SHAPE;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+    const int group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (partition_size % block_size != 0) return PA_ERR_SHAPE;
+    if ((long long)max_blocks_per_seq * block_size < (long long)max_seq_len) return PA_ERR_SHAPE;
+    const int max_parts = num_partitions(max_seq_len, partition_size);
+    if (max_parts > 65535) return PA_ERR_SHAPE;
+    if ((long long)num_seqs * num_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    pr.nothing_to_do = num_seqs == 0;
+    if (pr.nothing_to_do) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
+    if (kv_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_parts);
+    if (need > 0 && !workspace) return PA_ERR_NULL;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return PA_ERR_SHAPE;
+
+    const size_t rows = (size_t)num_seqs * num_heads * max_parts;
+    DecodeArgs& a = pr.args;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.max_seq_len = max_seq_len;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.qk_scale_log2 = scale * kLog2e;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.partition_size = partition_size;
+    a.max_partitions = max_parts;
+    a.part_m = (float*)workspace;
+    a.part_l = (float*)((char*)workspace + align256(rows * 4));
+    a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
+    pr.head_dim = head_dim;
+    pr.group = group;
+    pr.kv_dtype = kv_dtype;
+    pr.q_dtype = q_dtype;
+    return PA_OK;
+}
+
+static int run_partition(const Prepared& pr, hipStream_t stream) {
+    if (pr.args.max_partitions == 0) return PA_OK;  // every sequence is empty
+    switch (pr.kv_dtype) {
+        case PA_DTYPE_F32: return launch_partition_f32(pr.args, pr.head_dim, pr.group, stream);
+        case PA_DTYPE_F16: return launch_partition_f16(pr.args, pr.head_dim, pr.group, stream);
+        case PA_DTYPE_BF16: return launch_partition_bf16(pr.args, pr.head_dim, pr.group, stream);
+        case PA_DTYPE_FP8_E4M3: return launch_partition_fp8_bf16q(pr.args, pr.head_dim, pr.group, stream);
+    }
+    return PA_ERR_DTYPE;
+}
+
+static int run_reduce(const Prepared& pr, hipStream_t stream) {
+    const dim3 grid((unsigned)(pr.args.num_seqs * pr.args.num_heads));
+    if (pr.head_dim == 128)
+        hipLaunchKernelGGL(decode_reduce_kernel<128>, grid, dim3(128), 0, stream, pr.args);
+    else
+        hipLaunchKernelGGL(decode_reduce_kernel<64>, grid, dim3(64), 0, stream, pr.args);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace pa
+
+#define PA_DECODE_PARAMS                                                                          \
+    void *out, int out_dtype, const void *q, int q_dtype, const void *k_cache, const void *v_cache, \
+        int kv_dtype, const int32_t *block_tables, int max_blocks_per_seq, const int32_t *seq_lens, \
+        int max_seq_len, int num_seqs, int num_heads, int num_kv_heads, int head_dim,             \
+        int block_size, int num_blocks, float scale, const float *k_scale, const float *v_scale,  \
+        int partition_size, void *workspace, size_t workspace_bytes, void *stream
+#define PA_DECODE_ARGS                                                                             \
+    out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,      \
+        seq_lens, max_seq_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, \
+        scale, k_scale, v_scale, partition_size, workspace, workspace_bytes
+
+extern "C" size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                           int max_seq_len, int partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size <= 0)
+        return 0;
+    return pa::workspace_bytes_for(num_seqs, num_heads, head_dim,
+                                   pa::num_partitions(max_seq_len, partition_size));
+}
+
+extern "C" int pa_decode_partition(PA_DECODE_PARAMS) {
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    return pa::run_partition(pr, (hipStream_t)stream);
+}
+
+extern "C" int pa_decode_reduce(PA_DECODE_PARAMS) {
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    return pa::run_reduce(pr, (hipStream_t)stream);
+}
+
+extern "C" int pa_decode(PA_DECODE_PARAMS) {
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    const int s1 = pa::run_partition(pr, (hipStream_t)stream);
+    if (s1 != PA_OK) return s1;
+    return pa::run_reduce(pr, (hipStream_t)stream);
+}

@@ -1,0 +1,567 @@
+// Split-KV paged decode attention for gfx950: the partition kernel.
+//
+// One workgroup per (sequence, kv head, KV partition); W wavefronts per
+// workgroup.  Wave w walks logical blocks w, w+W, w+2W, ... of the
+// partition.  For each block it copies the (block, kv head) K tile and V
+// tile (block_size x head_dim elements each, contiguous in the pool) from
+// global memory straight into its own S-stage LDS ring with 16-byte
+// asynchronous copies (global_load_lds_dwordx4), S-1 blocks ahead of the
+// block it computes on, so several KiB per wave stay in flight without
+// holding registers.  The physical block id is read once per block, with a
+// scalar load, when the block's copy is issued.
+//
+// Register layout of the compute: lane l handles token row r = l / LPR of
+// every group of R = 64/LPR rows and the 8 elements of "column" c = l % LPR
+// of that row (LPR = head_dim / 8).  Each K row is therefore spread over
+// LPR consecutive lanes of one DPP row, so a q.k dot product is a per-lane
+// partial (dot2 instructions for 16-bit data) followed by a 3- or 4-step DPP
+// butterfly that leaves the full score in every lane of the group.  The V
+// row sits in the same lanes, so the score a lane holds is exactly the
+// weight it needs for its V elements: no score exchange is required.  All
+// G query heads of the kv head are computed from the same LDS tile (the
+// tile is loaded once per workgroup and shared across the GQA group).
+//
+// Every lane keeps an online-softmax state (m, l, acc[8]) per query head
+// for its row subset, updated per 16-token chunk with the recurrence
+//     m' = max(m, max_j s_j); alpha = 2^(m - m'); l' = alpha l + sum_j 2^(s_j - m');
+//     acc' = alpha acc + sum_j 2^(s_j - m') v_j
+// (scores are pre-multiplied by log2 e, so base-2 exponentials give the
+// natural-base softmax).  At the end the row subsets of a wave are merged
+// with cross-lane shuffles and the waves of the workgroup through LDS, using
+// the same rule; the merged (m, l, acc) goes to the workspace, or, when the
+// sequence has a single partition, acc / l goes straight to the output.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_common.hpp"
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+    void* out;
+    int out_dtype;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    int max_blocks_per_seq;
+    const int32_t* seq_lens;
+    int max_seq_len;
+    int num_seqs;
+    int num_heads;
+    int num_kv_heads;
+    int block_size;
+    int num_blocks;
+    float qk_scale_log2;  // scale * log2(e)
+    const float* k_scale;
+    const float* v_scale;
+    int partition_size;
+    int max_partitions;
+    float* part_m;    // [num_seqs][num_heads][max_partitions]
+    float* part_l;    // [num_seqs][num_heads][max_partitions]
+    float* part_acc;  // [num_seqs][num_heads][max_partitions][head_dim]
+};
+
+__device__ __forceinline__ void store_out(void* out, int dtype, size_t idx, float v) {
+    if (dtype == PA_DTYPE_F32)
+        ((float*)out)[idx] = v;
+    else if (dtype == PA_DTYPE_BF16)
+        ((uint16_t*)out)[idx] = f32_to_bf16_bits(v);
+    else
+        ((_Float16*)out)[idx] = (_Float16)v;
+}
+
+// Placement of a lane's 8 elements inside one token row of format KV.
+template <Fmt KV, int D>
+struct LaneRow {
+    static constexpr int EB = FmtBytes<KV>::value;
+    static constexpr int LPR = D / 8;
+    static constexpr int NW = 2 * EB;  // 32-bit words that hold 8 elements
+
+    // 4-byte elements take two 16-byte pieces (c and c + LPR) so that each
+    // load instruction of the wave covers consecutive 16-byte granules.
+    __device__ static __forceinline__ int dim(int c, int e) {
+        if constexpr (EB == 4)
+            return e < 4 ? c * 4 + e : (c + LPR) * 4 + (e - 4);
+        else
+            return c * 8 + e;
+    }
+
+    __device__ static __forceinline__ void load(const char* row, int c, uint32_t (&w)[NW]) {
+        if constexpr (EB == 4) {
+            const u32x4 a = *(const u32x4*)(row + c * 16);
+            const u32x4 b = *(const u32x4*)(row + (c + LPR) * 16);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else if constexpr (EB == 2) {
+            const u32x4 a = *(const u32x4*)(row + c * 16);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        } else {
+            const u32x2 a = *(const u32x2*)(row + c * 8);
+            w[0] = a.x; w[1] = a.y;
+        }
+    }
+
+    // The 8 elements as float32 (unscaled FP8 codes for FP8).
+    __device__ static __forceinline__ void to_f32(const uint32_t (&w)[NW], float (&v)[8]) {
+        if constexpr (KV == Fmt::F32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(w[e]);
+        } else if constexpr (KV == Fmt::BF16) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) { v[2 * p] = bf16_lo(w[p]); v[2 * p + 1] = bf16_hi(w[p]); }
+        } else if constexpr (KV == Fmt::F16) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) { v[2 * p] = f16_lo(w[p]); v[2 * p + 1] = f16_hi(w[p]); }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[p], false);
+                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[p], true);
+                v[4 * p] = a.x; v[4 * p + 1] = a.y; v[4 * p + 2] = b.x; v[4 * p + 3] = b.y;
+            }
+        }
+    }
+};
+
+// Query operand of one head (lane's 8 elements) and the q.k partial product.
+template <Fmt KV, Fmt Q>
+struct QK;
+
+template <>
+struct QK<Fmt::F32, Fmt::F32> {
+    struct Op {
+        float x[8];
+        __device__ __forceinline__ void pin() {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(x[e]));
+        }
+    };
+    using KOp = Op;
+    template <int D>
+    __device__ static __forceinline__ Op load_q(const char* qrow, int c) {
+        constexpr int LPR = D / 8;
+        const float4 a = *(const float4*)(qrow + c * 16);
+        const float4 b = *(const float4*)(qrow + (c + LPR) * 16);
+        return Op{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+    }
+    __device__ static __forceinline__ KOp prep_k(const uint32_t (&w)[8]) {
+        KOp k;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k.x[e] = __uint_as_float(w[e]);
+        return k;
+    }
+    __device__ static __forceinline__ float dot(const Op& q, const KOp& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(q.x[e], k.x[e], s);
+        return s;
+    }
+};
+
+struct Packed16Op {
+    uint32_t w[4];
+    __device__ __forceinline__ void pin() {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) asm volatile("" : "+v"(w[p]));
+    }
+};
+
+template <>
+struct QK<Fmt::BF16, Fmt::BF16> {
+    using Op = Packed16Op;
+    using KOp = Packed16Op;
+    template <int D>
+    __device__ static __forceinline__ Op load_q(const char* qrow, int c) {
+        const u32x4 a = *(const u32x4*)(qrow + c * 16);
+        return Op{{a.x, a.y, a.z, a.w}};
+    }
+    __device__ static __forceinline__ KOp prep_k(const uint32_t (&w)[4]) { return KOp{{w[0], w[1], w[2], w[3]}}; }
+    __device__ static __forceinline__ float dot(const Op& q, const KOp& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w[p]),
+                                                __builtin_bit_cast(bf16x2, k.w[p]), s, false);
+        return s;
+    }
+};
+
+template <>
+struct QK<Fmt::F16, Fmt::F16> {
+    using Op = Packed16Op;
+    using KOp = Packed16Op;
+    template <int D>
+    __device__ static __forceinline__ Op load_q(const char* qrow, int c) {
+        const u32x4 a = *(const u32x4*)(qrow + c * 16);
+        return Op{{a.x, a.y, a.z, a.w}};
+    }
+    __device__ static __forceinline__ KOp prep_k(const uint32_t (&w)[4]) { return KOp{{w[0], w[1], w[2], w[3]}}; }
+    __device__ static __forceinline__ float dot(const Op& q, const KOp& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.w[p]), __builtin_bit_cast(f16x2, k.w[p]), s,
+                                       false);
+        return s;
+    }
+};
+
+// FP8 keys are widened to bfloat16 pairs (exact: every E4M3 value is a
+// bfloat16 value) once per row and shared by all G heads.
+template <>
+struct QK<Fmt::FP8, Fmt::BF16> {
+    using Op = Packed16Op;
+    using KOp = Packed16Op;
+    template <int D>
+    __device__ static __forceinline__ Op load_q(const char* qrow, int c) {
+        const u32x4 a = *(const u32x4*)(qrow + c * 16);
+        return Op{{a.x, a.y, a.z, a.w}};
+    }
+    __device__ static __forceinline__ KOp prep_k(const uint32_t (&w)[2]) {
+        KOp k;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            k.w[2 * p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[p], 1.0f, false));
+            k.w[2 * p + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[p], 1.0f, true));
+        }
+        return k;
+    }
+    __device__ static __forceinline__ float dot(const Op& q, const KOp& k) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w[p]),
+                                                __builtin_bit_cast(bf16x2, k.w[p]), s, false);
+        return s;
+    }
+};
+
+template <Fmt KV, int D, int BS, int G, int W, int S>
+struct PartitionShape {
+    static constexpr int EB = FmtBytes<KV>::value;
+    static constexpr int LPR = D / 8;
+    static constexpr int R = 64 / LPR;
+    static constexpr int ROWB = D * EB;
+    static constexpr int TILE = BS * ROWB;
+    static constexpr int DMA_PER_TILE = TILE / 1024;
+    static constexpr int DMA_PER_BLOCK = 2 * DMA_PER_TILE;
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int RING = S * STAGE;  // per wave
+    static constexpr int PASSES = 16 / R;   // row groups per 16-token chunk
+    static constexpr int CHUNKS = BS / 16;
+    // cross-wave merge area: m[W][G], l[W][G], invalid[W] (padded), acc[W][G][D]
+    static constexpr int MERGE_HEAD = ((2 * W * G + W) * 4 + 15) / 16 * 16;
+    static constexpr int MERGE = W > 1 ? MERGE_HEAD + W * G * D * 4 : 0;
+    static constexpr int LDS = (W * RING > MERGE) ? W * RING : MERGE;
+    static_assert(TILE % 1024 == 0, "a tile must be a whole number of 1 KiB wave copies");
+    static_assert((S - 1) * DMA_PER_BLOCK <= 63, "vmcnt can count at most 63 copies");
+    static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+};
+
+template <int PER_BLOCK, int S>
+__device__ __forceinline__ void wait_blocks_in_flight(int n) {
+    // at most n whole blocks (n <= S-1) may still be copying
+    if constexpr (S >= 4) { if (n >= 3) { wait_vmcnt<3 * PER_BLOCK>(); return; } }
+    if constexpr (S >= 3) { if (n >= 2) { wait_vmcnt<2 * PER_BLOCK>(); return; } }
+    if constexpr (S >= 2) { if (n >= 1) { wait_vmcnt<PER_BLOCK>(); return; } }
+    wait_vmcnt<0>();
+}
+
+template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S>
+__global__ void __launch_bounds__(W * 64)
+decode_partition_kernel(const DecodeArgs a) {
+    using Sh = PartitionShape<KV, D, BS, G, W, S>;
+    using Row = LaneRow<KV, D>;
+    using Dot = QK<KV, Q>;
+    constexpr int LPR = Sh::LPR, R = Sh::R, ROWB = Sh::ROWB, TILE = Sh::TILE;
+    constexpr int QB = FmtBytes<Q>::value;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+    const int seq = blockIdx.x / a.num_kv_heads;
+    const int kvh = blockIdx.x - seq * a.num_kv_heads;
+    const int part = blockIdx.y;
+
+    const int T = a.seq_lens[seq];
+    if (T <= 0 || T > a.max_seq_len) return;  // empty or invalid rows: written by the reduce kernel
+    if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
+    const int P = a.partition_size;
+    const int n_parts = (T + P - 1) / P;
+    if (part >= n_parts) return;
+
+    const int tok0 = part * P;
+    const int tok1 = min(tok0 + P, T);
+    const int lb0 = tok0 / BS;
+    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    const int nbw = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    const int hq0 = kvh * G;
+
+    // Query operands of the G heads (the lane's 8 elements of each).
+    typename Dot::Op qop[G];
+    {
+        const char* qbase = (const char*)a.q + ((size_t)seq * a.num_heads + hq0) * D * QB;
+#pragma unroll
+        for (int g = 0; g < G; ++g) qop[g] = Dot::template load_q<D>(qbase + (size_t)g * D * QB, c);
+        // make the queries resident before any asynchronous copy is queued, so
+        // the compiler's own wait for them cannot also wait for the copies
+#pragma unroll
+        for (int g = 0; g < G; ++g) qop[g].pin();
+    }
+    float qk_scale = a.qk_scale_log2;
+    if constexpr (KV == Fmt::FP8) qk_scale *= a.k_scale[kvh];
+
+    const char* kc = (const char*)a.k_cache;
+    const char* vc = (const char*)a.v_cache;
+    char* ring = smem + wave * Sh::RING;
+    const uint32_t ring_lds = lds_addr_of(smem) + (uint32_t)(wave * Sh::RING);
+    int invalid = 0;
+
+    auto issue = [&](int k, int stage) {
+        const int lb = lb0 + wave + k * W;
+        int pb = bt[lb];
+        if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
+        const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)lane * 16;
+        const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
+#pragma unroll
+        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds(kc + tile + i * 1024, dst + i * 1024);
+#pragma unroll
+        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds(vc + tile + i * 1024, dst + TILE + i * 1024);
+    };
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    }
+
+    // One 16-token chunk of a staged block.  MASKED: the block may hold rows
+    // at or beyond T (only the sequence's last block), whose scores become
+    // -inf and whose values are ignored.
+    auto chunk = [&](const char* kb, int row_tok0, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const char* vb = kb + TILE;
+        float s[Sh::PASSES][G];
+        float v[Sh::PASSES][8];
+#pragma unroll
+        for (int j = 0; j < Sh::PASSES; ++j) {
+            uint32_t kw[Row::NW];
+            Row::load(kb + (j * R + r) * ROWB, c, kw);
+            const auto kop = Dot::prep_k(kw);
+#pragma unroll
+            for (int g = 0; g < G; ++g) s[j][g] = group_sum<LPR>(Dot::dot(qop[g], kop));
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::PASSES; ++j) {
+            uint32_t vw[Row::NW];
+            Row::load(vb + (j * R + r) * ROWB, c, vw);
+            Row::to_f32(vw, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::PASSES; ++j) {
+            const bool ok = !MASKED || (row_tok0 + j * R + r < T);
+#pragma unroll
+            for (int g = 0; g < G; ++g) s[j][g] = ok ? s[j][g] * qk_scale : -INFINITY;
+            if constexpr (MASKED) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[j][e] = ok ? v[j][e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float mx = s[0][g];
+#pragma unroll
+            for (int j = 1; j < Sh::PASSES; ++j) mx = fmaxf(mx, s[j][g]);
+            const float mn = fmaxf(m[g], mx);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = fast_exp2(m[g] - mu);
+            float p[Sh::PASSES];
+            float psum = 0.f;
+#pragma unroll
+            for (int j = 0; j < Sh::PASSES; ++j) { p[j] = fast_exp2(s[j][g] - mu); psum += p[j]; }
+            l[g] = fmaf(l[g], alpha, psum);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float t = acc[g][e] * alpha;
+#pragma unroll
+                for (int j = 0; j < Sh::PASSES; ++j) t = fmaf(p[j], v[j][e], t);
+                acc[g][e] = t;
+            }
+            m[g] = mn;
+        }
+    };
+
+    // ---- main loop: S-stage ring, S-1 blocks of copies ahead of compute
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        if (k < nbw) issue(k, k);
+    int stage = 0;
+    for (int k = 0; k < nbw; ++k) {
+        if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
+        wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S>(min(S - 1, nbw - 1 - k));
+        const char* kb = ring + stage * Sh::STAGE;
+        const int blk_tok0 = (lb0 + wave + k * W) * BS;
+        if (blk_tok0 + BS <= T) {
+#pragma unroll
+            for (int ch = 0; ch < Sh::CHUNKS; ++ch)
+                chunk(kb + ch * 16 * ROWB, blk_tok0 + ch * 16, std::false_type{});
+        } else {
+#pragma unroll
+            for (int ch = 0; ch < Sh::CHUNKS; ++ch)
+                chunk(kb + ch * 16 * ROWB, blk_tok0 + ch * 16, std::true_type{});
+        }
+        stage = stage + 1 == S ? 0 : stage + 1;
+    }
+
+    // ---- merge the row subsets of this wave (lanes l, l^LPR, l^2LPR, ...)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m[g], off);
+            const float lo = __shfl_xor(l[g], off);
+            const float mn = fmaxf(m[g], mo);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float f0 = fast_exp2(m[g] - mu);
+            const float f1 = fast_exp2(mo - mu);
+            l[g] = l[g] * f0 + lo * f1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] * f0 + __shfl_xor(acc[g][e], off) * f1;
+            m[g] = mn;
+        }
+    }
+
+    const float vs = KV == Fmt::FP8 ? a.v_scale[kvh] : 1.f;
+    auto emit = [&](int g, int d, float M, float L, float A, int bad) {
+        const int hq = hq0 + g;
+        const size_t row = (size_t)seq * a.num_heads + hq;
+        if (n_parts == 1) {
+            store_out(a.out, a.out_dtype, row * D + d, bad ? __builtin_nanf("") : A / L * vs);
+        } else {
+            const size_t pidx = row * a.max_partitions + part;
+            if (d == 0) {
+                a.part_m[pidx] = bad ? __builtin_nanf("") : M;
+                a.part_l[pidx] = bad ? __builtin_nanf("") : L;
+            }
+            a.part_acc[pidx * D + d] = bad ? __builtin_nanf("") : A * vs;
+        }
+    };
+
+    if constexpr (W == 1) {
+        if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) emit(g, Row::dim(c, e), m[g], l[g], acc[g][e], invalid);
+        }
+    } else {
+        __syncthreads();  // every wave is done with its ring; reuse the LDS for the merge
+        float* wm = (float*)smem;
+        float* wl = wm + W * G;
+        int* winv = (int*)(wl + W * G);
+        float* wacc = (float*)(smem + Sh::MERGE_HEAD);
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) { wm[wave * G + g] = m[g]; wl[wave * G + g] = l[g]; }
+            winv[wave] = invalid;
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * D + Row::dim(c, e)] = acc[g][e];
+        }
+        __syncthreads();
+        int bad = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) bad |= winv[w];
+        for (int o = threadIdx.x; o < G * D; o += W * 64) {
+            const int g = o / D;
+            const int d = o - g * D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + g]);
+            const float mu = M == -INFINITY ? 0.f : M;
+            float L = 0.f, A = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float f = fast_exp2(wm[w * G + g] - mu);
+                L = fmaf(f, wl[w * G + g], L);
+                A = fmaf(f, wacc[(w * G + g) * D + d], A);
+            }
+            emit(g, d, M, L, A, bad);
+        }
+    }
+}
+
+// Launch one partition-kernel instantiation (sets the LDS attribute once).
+template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S>
+int launch_partition(const DecodeArgs& a, hipStream_t stream) {
+    using Sh = PartitionShape<KV, D, BS, G, W, S>;
+    auto kernel = decode_partition_kernel<KV, Q, D, BS, G, W, S>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+    if (attr != hipSuccess) return PA_ERR_LAUNCH;
+    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.max_partitions);
+    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// Per-format dispatch over head_dim, block_size and group size; defined in
+// one translation unit per KV format.
+int launch_partition_f32(const DecodeArgs& a, int head_dim, int group, hipStream_t stream);
+int launch_partition_f16(const DecodeArgs& a, int head_dim, int group, hipStream_t stream);
+int launch_partition_bf16(const DecodeArgs& a, int head_dim, int group, hipStream_t stream);
+int launch_partition_fp8_bf16q(const DecodeArgs& a, int head_dim, int group, hipStream_t stream);
+
+// Waves per workgroup and ring depth of the default variant.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_STAGES
+#define PA_DECODE_STAGES 2
+#endif
+
+// Waves per workgroup for a shape: the default, halved until the rings of
+// all waves fit in 96 KiB of LDS.
+template <Fmt KV, int D, int BS, int S>
+constexpr int waves_for() {
+    int w = PA_DECODE_WAVES;
+    while (w > 1 && w * S * 2 * BS * D * FmtBytes<KV>::value > 96 * 1024) w /= 2;
+    return w;
+}
+
+template <Fmt KV, Fmt Q, int D, int BS>
+int dispatch_group(const DecodeArgs& a, int group, hipStream_t stream) {
+    constexpr int S = PA_DECODE_STAGES;
+    constexpr int W = waves_for<KV, D, BS, S>();
+    switch (group) {
+        case 1: return launch_partition<KV, Q, D, BS, 1, W, S>(a, stream);
+        case 2: return launch_partition<KV, Q, D, BS, 2, W, S>(a, stream);
+        case 4: return launch_partition<KV, Q, D, BS, 4, W, S>(a, stream);
+        case 8: return launch_partition<KV, Q, D, BS, 8, W, S>(a, stream);
+    }
+    return PA_ERR_UNSUPPORTED;
+}
+
+#define PA_DEFINE_PARTITION_DISPATCH(NAME, KVF, QF)                                  \
+    int NAME(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {     \
+        const int bs = a.block_size;                                                 \
+        if (head_dim == 128 && bs == 16) return dispatch_group<KVF, QF, 128, 16>(a, group, stream); \
+        if (head_dim == 128 && bs == 32) return dispatch_group<KVF, QF, 128, 32>(a, group, stream); \
+        if (head_dim == 64 && bs == 16) return dispatch_group<KVF, QF, 64, 16>(a, group, stream);   \
+        if (head_dim == 64 && bs == 32) return dispatch_group<KVF, QF, 64, 32>(a, group, stream);   \
+        return PA_ERR_UNSUPPORTED;                                                   \
+    }
+
+}  // namespace pa

@@ -83,18 +83,51 @@ def pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partiti
     return int(_lib.load().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partition_size))
 
 
-def _decode_call(name, out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale,
-                 partition_size, workspace, k_scale=None, v_scale=None, kv_dtype=None, q_dtype=None,
-                 out_dtype=None, stream=None):
+def _decode_argv(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, partition_size,
+                 workspace, k_scale=None, v_scale=None, kv_dtype=None, q_dtype=None, out_dtype=None, stream=None):
     num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
     num_seqs, num_heads, _ = q.shape
-    fn = getattr(_lib.load(), name)
-    _check(fn(_ptr(out), dtype_code(out, out_dtype), _ptr(q), dtype_code(q, q_dtype), _ptr(k_cache),
-              _ptr(v_cache), dtype_code(k_cache, kv_dtype), _ptr(block_tables), int(block_tables.shape[1]),
-              _ptr(seq_lens), int(max_seq_len), num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-              num_blocks, float(scale), _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace),
-              int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
-              _stream(stream, q.device)), name)
+    return (_ptr(out), dtype_code(out, out_dtype), _ptr(q), dtype_code(q, q_dtype), _ptr(k_cache), _ptr(v_cache),
+            dtype_code(k_cache, kv_dtype), _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
+            int(max_seq_len), num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, float(scale),
+            _ptr(k_scale), _ptr(v_scale), int(partition_size), _ptr(workspace),
+            int(workspace.numel() * workspace.element_size()) if workspace is not None else 0,
+            _stream(stream, q.device))
+
+
+def prepared(name, *args, **kw):
+    """A zero-argument callable that issues the C call ``name`` with these
+    arguments, marshalled once (for loops that repeat an identical call).
+
+    The tensors must stay alive and in place while the callable is used.
+    """
+    lib = _lib.load()
+    fn = getattr(lib, name)
+    if name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
+        argv = _decode_argv(*args, **kw)
+    elif name == "pa_reshape_and_cache":
+        key, value, k_cache, v_cache, slot_mapping = args
+        nb, hkv, bs, d = k_cache.shape
+        argv = (_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.numel()),
+                hkv, d, bs, nb, dtype_code(k_cache, kw.get("kv_dtype")), _stream(kw.get("stream"), k_cache.device))
+    elif name == "pa_copy_blocks":
+        k_cache, v_cache, block_pairs = args
+        nb, hkv, bs, d = k_cache.shape
+        argv = (_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), int(block_pairs.numel() // 2), hkv, d, bs, nb,
+                dtype_code(k_cache, kw.get("kv_dtype")), _stream(kw.get("stream"), k_cache.device))
+    else:
+        raise ValueError(name)
+    c_args = [t(a) if a is not None else None for t, a in zip(fn.argtypes, argv)]
+
+    def call():
+        status = fn(*c_args)
+        if status != 0:
+            raise PagedAttnError(status, name)
+    return call
+
+
+def _decode_call(name, *args, **kw):
+    _check(getattr(_lib.load(), name)(*_decode_argv(*args, **kw)), name)
 
 
 def pa_decode(*args, **kw):

@@ -31,11 +31,16 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load the shared library once and attach the C signatures."""
+def load(path: str = None):
+    """Load the shared library once and attach the C signatures.
+
+    ``PAGEDATTN_LIBRARY`` in the environment names another build of the
+    same ABI (for example a tuning variant); the default is the in-tree one.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("PAGEDATTN_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m paged_kv_cache_142_amd.build` "

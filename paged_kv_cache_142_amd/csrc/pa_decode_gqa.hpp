@@ -1,0 +1,353 @@
+// Partition kernel for query-head groups of G = 4 with 16-bit KV (bf16/fp16).
+//
+// Same decomposition, staging and merge as decode_partition_kernel (one
+// workgroup per (sequence, kv head, KV partition); each wave streams its
+// blocks' K/V tiles into a private LDS ring with asynchronous 16-byte
+// copies), but the score step puts the G query heads into lanes instead of
+// reducing every dot product across lanes:
+//
+//   score layout   lane = (head h, token tq, half), tq fastest:
+//                  lane = h*16 + half*8 + tq.  The lane holds head h's query
+//                  elements of its half of the row (64 dims) and computes the
+//                  half dot product for token tq of the pass; one DPP
+//                  rotate-add joins the two halves.  Two passes of 8 tokens
+//                  cover a 16-token chunk.  The G heads read the same K rows
+//                  (LDS broadcast), so each staged tile serves the whole group.
+//   K tile in LDS  XOR-swizzled by 16-byte granule: row t's granule g lives
+//                  at granule t*NG + (g ^ (t mod NG)).  The copy engine writes
+//                  lane l's 16 bytes at granule l of each 1 KiB copy, so the
+//                  swizzle is applied by choosing each lane's source address;
+//                  reads of 8 different rows at one logical granule then hit
+//                  8 different bank groups.
+//   softmax        the running max m and sum l are per head and uniform over
+//                  the wave: per chunk a 3-step DPP max and sum over the 8
+//                  token lanes of the head, one exp2 per score and one for the
+//                  rescale factor alpha = 2^(m - m').
+//   value layout   as in decode_partition_kernel (lane = token row r, column
+//                  c of 8 elements, all G heads per lane); p[t][h] and alpha[h]
+//                  reach it through a 272-byte per-wave LDS scratch.  acc is
+//                  rescaled only when some head's max moved (wave-uniform test).
+//
+// At the end the R row subsets and W waves are summed through LDS (the row
+// subsets share the wave's per-head max; waves are merged with the
+// log-sum-exp rule).
+#pragma once
+
+#include "pa_decode_kernel.hpp"
+
+namespace pa {
+
+template <Fmt KV, int D, int BS, int W, int S>
+struct GqaShape {
+    static constexpr int G = 4;
+    static constexpr int EB = 2;
+    static constexpr int NG = D * EB / 16;   // 16-byte granules per token row
+    static constexpr int ROWB = D * EB;
+    static constexpr int TILE = BS * ROWB;
+    static constexpr int DMA_PER_TILE = TILE / 1024;
+    static constexpr int DMA_PER_BLOCK = 2 * DMA_PER_TILE;
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int TQ = 8;             // tokens per score pass
+    static constexpr int HALF_G = NG / 2;    // granules per half row
+    static constexpr int QW = HALF_G * 4;    // 32-bit query words per lane
+    static constexpr int NPASS = 16 / TQ;
+    static constexpr int R = 64 / NG;        // value-layout token rows per pass
+    static constexpr int VPASS = 16 / R;
+    static constexpr int SCRATCH = 512;      // p[16][G] + alpha[G], padded
+    static constexpr int RING = S * STAGE + SCRATCH;
+    static constexpr int MERGE_HEAD = ((2 * W * G + W) * 4 + 15) / 16 * 16;
+    static constexpr int MERGE = MERGE_HEAD + W * R * G * D * 4;
+    static constexpr int LDS = (W * RING > MERGE) ? W * RING : MERGE;
+    static_assert(TILE % 1024 == 0, "a tile must be a whole number of 1 KiB wave copies");
+    static_assert((S - 1) * DMA_PER_BLOCK <= 63, "vmcnt can count at most 63 copies");
+    static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+    static_assert(G * 2 * TQ == 64, "lane decomposition");
+};
+
+template <Fmt KV>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float c) {
+    if constexpr (KV == Fmt::BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                               false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true)));
+}
+
+template <Fmt KV, int D, int BS, int W, int S>
+__global__ void __launch_bounds__(W * 64)
+decode_partition_gqa4_kernel(const DecodeArgs a) {
+    using Sh = GqaShape<KV, D, BS, W, S>;
+    using Row = LaneRow<KV, D>;
+    constexpr int G = Sh::G, NG = Sh::NG, ROWB = Sh::ROWB, TILE = Sh::TILE, TQ = Sh::TQ, R = Sh::R;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // score layout
+    const int tq = lane & (TQ - 1);
+    const int half = (lane >> 3) & 1;
+    const int hl = lane >> 4;
+    // value layout
+    const int r = lane / NG;
+    const int c = lane % NG;
+
+    const int seq = blockIdx.x / a.num_kv_heads;
+    const int kvh = blockIdx.x - seq * a.num_kv_heads;
+    const int part = blockIdx.y;
+    const int T = a.seq_lens[seq];
+    if (T <= 0 || T > a.max_seq_len) return;
+    if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
+    const int P = a.partition_size;
+    const int n_parts = (T + P - 1) / P;
+    if (part >= n_parts) return;
+    const int tok0 = part * P;
+    const int tok1 = min(tok0 + P, T);
+    const int lb0 = tok0 / BS;
+    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    // this wave's blocks: a contiguous, balanced share of the partition
+    const int kb0 = nblk * wave / W;
+    const int nbw = nblk * (wave + 1) / W - kb0;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0 + kb0;
+    // physical ids of the wave's blocks, one per lane (64 at a time); read
+    // with readlane when a block's copy is issued
+    int ids = lane < nbw ? bt[lane] : 0;
+    const int hq0 = kvh * G;
+
+    // Query words of this lane's head and half row.
+    uint32_t qw[Sh::QW];
+    {
+        const char* qrow = (const char*)a.q + (((size_t)seq * a.num_heads + hq0 + hl) * D + half * (D / 2)) * 2;
+#pragma unroll
+        for (int i = 0; i < Sh::HALF_G; ++i) {
+            const u32x4 v = *(const u32x4*)(qrow + i * 16);
+            qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < Sh::QW; ++i) asm volatile("" : "+v"(qw[i]));
+    }
+    const float qk_scale = a.qk_scale_log2;
+
+    // Source offset of this lane's 16 bytes in each 1 KiB copy of a K tile
+    // (swizzled) and a V tile (natural order); the same for every block.
+    uint32_t koff[Sh::DMA_PER_TILE];
+#pragma unroll
+    for (int j = 0; j < Sh::DMA_PER_TILE; ++j) {
+        const int pos = 64 * j + lane;
+        const int t = pos / NG;
+        const int g = (pos % NG) ^ (t & (NG - 1));
+        koff[j] = (uint32_t)(t * ROWB + g * 16);
+    }
+
+    const char* kc = (const char*)a.k_cache;
+    const char* vc = (const char*)a.v_cache;
+    char* ring = smem + wave * Sh::RING;
+    float* p_lds = (float*)(ring + S * Sh::STAGE);  // [16][G]
+    float* alpha_lds = p_lds + 16 * G;                   // [G]
+    const uint32_t ring_lds = lds_addr_of(smem) + (uint32_t)(wave * Sh::RING);
+    int invalid = 0;
+
+    auto issue = [&](int k, int stage) {
+        if (k > 0 && (k & 63) == 0) ids = k + lane < nbw ? bt[k + lane] : 0;
+        int pb = __builtin_amdgcn_readlane(ids, k & 63);
+        if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
+        const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
+        const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
+#pragma unroll
+        for (int j = 0; j < Sh::DMA_PER_TILE; ++j) dma16_to_lds(kc + tile + koff[j], dst + j * 1024);
+#pragma unroll
+        for (int j = 0; j < Sh::DMA_PER_TILE; ++j)
+            dma16_to_lds(vc + tile + (size_t)j * 1024 + lane * 16, dst + TILE + j * 1024);
+    };
+
+    float m = -INFINITY, l = 0.f;  // per head hl (uniform over its 16 lanes)
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+
+    auto chunk = [&](const char* stage_ptr, int ch, int row_tok0, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        // ---- scores: lane (hl, half, tq), passes of TQ tokens
+        float s[Sh::NPASS];
+#pragma unroll
+        for (int p = 0; p < Sh::NPASS; ++p) {
+            const int t = ch * 16 + p * TQ + tq;  // row inside the block
+            const char* rowp = stage_ptr + t * ROWB;
+            float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < Sh::HALF_G; ++i) {
+                const int g = half * Sh::HALF_G + i;
+                const u32x4 kv = *(const u32x4*)(rowp + ((g ^ (t & (NG - 1))) * 16));
+                float& cc = (i & 1) ? c1 : c0;
+                cc = dot2_acc<KV>(qw[4 * i], kv.x, cc);
+                cc = dot2_acc<KV>(qw[4 * i + 1], kv.y, cc);
+                cc = dot2_acc<KV>(qw[4 * i + 2], kv.z, cc);
+                cc = dot2_acc<KV>(qw[4 * i + 3], kv.w, cc);
+            }
+            float sp = c0 + c1;
+            sp += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sp), 0x128, 0xf, 0xf, true));  // row_ror:8
+            sp *= qk_scale;
+            if constexpr (MASKED) sp = (row_tok0 + p * TQ + tq < T) ? sp : -INFINITY;
+            s[p] = sp;
+        }
+        // ---- online softmax per head (the 8 token lanes of each half agree)
+        float mx = s[0];
+#pragma unroll
+        for (int p = 1; p < Sh::NPASS; ++p) mx = fmaxf(mx, s[p]);
+        mx = dpp_max<0xB1>(mx);
+        mx = dpp_max<0x4E>(mx);
+        mx = dpp_max<0x141>(mx);
+        const float mn = fmaxf(m, mx);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m - mu);
+        float psum = 0.f;
+        float pv[Sh::NPASS];
+#pragma unroll
+        for (int p = 0; p < Sh::NPASS; ++p) { pv[p] = fast_exp2(s[p] - mu); psum += pv[p]; }
+        psum = group_sum<8>(psum);
+        l = fmaf(l, alpha, psum);
+        const bool moved = mn != m;
+        m = mn;
+        if (half == 0) {
+#pragma unroll
+            for (int p = 0; p < Sh::NPASS; ++p) p_lds[(p * TQ + tq) * G + hl] = pv[p];
+            if (tq == 0) alpha_lds[hl] = alpha;
+        }
+        const bool rescale = __builtin_amdgcn_ballot_w64(moved) != 0;
+        // ---- values: lane (r, c), all heads
+        const char* vb = stage_ptr + TILE + ch * 16 * ROWB;
+        if (rescale) {
+            const float4 al = *(const float4*)alpha_lds;
+            const float alg[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] *= alg[g];
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::VPASS; ++j) {
+            const int tr = j * R + r;
+            const float4 pp = *(const float4*)(p_lds + tr * G);
+            uint32_t vw[Row::NW];
+            Row::load(vb + tr * ROWB, c, vw);
+            float v[8];
+            Row::to_f32(vw, v);
+            if constexpr (MASKED) {
+                const bool ok = row_tok0 + tr < T;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = ok ? v[e] : 0.f;
+            }
+            const float pg[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pg[g], v[e], acc[g][e]);
+        }
+    };
+
+    // ---- main loop
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        if (k < nbw) issue(k, k);
+    int stage = 0;
+    for (int k = 0; k < nbw; ++k) {
+        if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
+        wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
+        const char* sp = ring + stage * Sh::STAGE;
+        const int blk_tok0 = (lb0 + kb0 + k) * BS;
+        if (blk_tok0 + BS <= T) {
+#pragma unroll
+            for (int ch = 0; ch < BS / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::false_type{});
+        } else {
+#pragma unroll
+            for (int ch = 0; ch < BS / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::true_type{});
+        }
+        stage = stage + 1 == S ? 0 : stage + 1;
+    }
+
+    // ---- merge: rows of a wave share its per-head max; waves by log-sum-exp
+    __syncthreads();
+    float* wm = (float*)smem;
+    float* wl = wm + W * G;
+    int* winv = (int*)(wl + W * G);
+    float* wacc = (float*)(smem + Sh::MERGE_HEAD);  // [W*R][G][D]
+    if (lane == 0) winv[wave] = invalid;
+    if (half == 0 && tq == 0) { wm[wave * G + hl] = m; wl[wave * G + hl] = l; }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wacc[((wave * R + r) * G + g) * D + Row::dim(c, e)] = acc[g][e];
+    __syncthreads();
+    int bad = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) bad |= winv[w];
+    const float vs = 1.f;
+    for (int o = threadIdx.x; o < G * D; o += W * 64) {
+        const int g = o / D;
+        const int d = o - g * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + g]);
+        const float mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = fast_exp2(wm[w * G + g] - mu);
+            float rows = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) rows += wacc[((w * R + rr) * G + g) * D + d];
+            L = fmaf(f, wl[w * G + g], L);
+            A = fmaf(f, rows, A);
+        }
+        const int hq = hq0 + g;
+        const size_t row = (size_t)seq * a.num_heads + hq;
+        if (n_parts == 1) {
+            store_out(a.out, a.out_dtype, row * D + d, bad ? __builtin_nanf("") : A / L * vs);
+        } else {
+            const size_t pidx = row * a.max_partitions + part;
+            if (d == 0) {
+                a.part_m[pidx] = bad ? __builtin_nanf("") : M;
+                a.part_l[pidx] = bad ? __builtin_nanf("") : L;
+            }
+            a.part_acc[pidx * D + d] = bad ? __builtin_nanf("") : A * vs;
+        }
+    }
+}
+
+template <Fmt KV, int D, int BS, int W, int S>
+int launch_partition_gqa4(const DecodeArgs& a, hipStream_t stream) {
+    using Sh = GqaShape<KV, D, BS, W, S>;
+    auto kernel = decode_partition_gqa4_kernel<KV, D, BS, W, S>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+    if (attr != hipSuccess) return PA_ERR_LAUNCH;
+    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.max_partitions);
+    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
+#ifndef PA_GQA_STAGES
+#define PA_GQA_STAGES 2
+#endif
+
+template <Fmt KV>
+int dispatch_gqa4(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+    constexpr int W = PA_GQA_WAVES, S = PA_GQA_STAGES;
+    const int bs = a.block_size;
+    if (head_dim == 128 && bs == 16) return launch_partition_gqa4<KV, 128, 16, W, S>(a, stream);
+    if (head_dim == 128 && bs == 32) return launch_partition_gqa4<KV, 128, 32, W, S>(a, stream);
+    if (head_dim == 64 && bs == 16) return launch_partition_gqa4<KV, 64, 16, W, S>(a, stream);
+    if (head_dim == 64 && bs == 32) return launch_partition_gqa4<KV, 64, 32, W, S>(a, stream);
+    return PA_ERR_UNSUPPORTED;
+}
+
+}  // namespace pa

@@ -262,13 +262,18 @@ struct PartitionShape {
     static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
 };
 
-template <int PER_BLOCK, int S>
+// Wait until at most n whole blocks (0 <= n <= N) of copies are in flight.
+template <int PER_BLOCK, int N>
 __device__ __forceinline__ void wait_blocks_in_flight(int n) {
-    // at most n whole blocks (n <= S-1) may still be copying
-    if constexpr (S >= 4) { if (n >= 3) { wait_vmcnt<3 * PER_BLOCK>(); return; } }
-    if constexpr (S >= 3) { if (n >= 2) { wait_vmcnt<2 * PER_BLOCK>(); return; } }
-    if constexpr (S >= 2) { if (n >= 1) { wait_vmcnt<PER_BLOCK>(); return; } }
-    wait_vmcnt<0>();
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= N) {
+            wait_vmcnt<N * PER_BLOCK>();
+            return;
+        }
+        wait_blocks_in_flight<PER_BLOCK, N - 1>(n);
+    }
 }
 
 template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S>
@@ -300,8 +305,13 @@ decode_partition_kernel(const DecodeArgs a) {
     const int tok1 = min(tok0 + P, T);
     const int lb0 = tok0 / BS;
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
-    const int nbw = nblk > wave ? (nblk - wave + W - 1) / W : 0;  // blocks of this wave
-    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
+    // this wave's blocks: a contiguous, balanced share of the partition
+    const int kb0 = nblk * wave / W;
+    const int nbw = nblk * (wave + 1) / W - kb0;
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0 + kb0;
+    // physical ids of the wave's blocks, one per lane (64 at a time); read
+    // with readlane when a block's copy is issued
+    int ids = lane < nbw ? bt[lane] : 0;
     const int hq0 = kvh * G;
 
     // Query operands of the G heads (the lane's 8 elements of each).
@@ -325,8 +335,8 @@ decode_partition_kernel(const DecodeArgs a) {
     int invalid = 0;
 
     auto issue = [&](int k, int stage) {
-        const int lb = lb0 + wave + k * W;
-        int pb = bt[lb];
+        if (k > 0 && (k & 63) == 0) ids = k + lane < nbw ? bt[k + lane] : 0;
+        int pb = __builtin_amdgcn_readlane(ids, k & 63);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)lane * 16;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
@@ -408,9 +418,9 @@ decode_partition_kernel(const DecodeArgs a) {
     int stage = 0;
     for (int k = 0; k < nbw; ++k) {
         if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
-        wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S>(min(S - 1, nbw - 1 - k));
+        wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
         const char* kb = ring + stage * Sh::STAGE;
-        const int blk_tok0 = (lb0 + wave + k * W) * BS;
+        const int blk_tok0 = (lb0 + kb0 + k) * BS;
         if (blk_tok0 + BS <= T) {
 #pragma unroll
             for (int ch = 0; ch < Sh::CHUNKS; ++ch)
@@ -532,18 +542,27 @@ int launch_partition_fp8_bf16q(const DecodeArgs& a, int head_dim, int group, hip
 #define PA_DECODE_STAGES 2
 #endif
 
-// Waves per workgroup for a shape: the default, halved until the rings of
-// all waves fit in 96 KiB of LDS.
+// Ring depth and waves per workgroup for a shape: the defaults, reduced
+// until the copies of S-1 blocks fit the vmcnt counter (63) and the rings of
+// all waves fit in the 160 KiB of LDS a workgroup may use.
+template <Fmt KV, int D, int BS>
+constexpr int stages_for() {
+    constexpr int stage = 2 * BS * D * FmtBytes<KV>::value;
+    int s = PA_DECODE_STAGES;
+    while (s > 2 && ((s - 1) * (stage / 1024) > 63 || s * stage > 160 * 1024)) --s;
+    return s;
+}
+
 template <Fmt KV, int D, int BS, int S>
 constexpr int waves_for() {
     int w = PA_DECODE_WAVES;
-    while (w > 1 && w * S * 2 * BS * D * FmtBytes<KV>::value > 96 * 1024) w /= 2;
+    while (w > 1 && w * S * 2 * BS * D * FmtBytes<KV>::value > 160 * 1024) w /= 2;
     return w;
 }
 
 template <Fmt KV, Fmt Q, int D, int BS>
 int dispatch_group(const DecodeArgs& a, int group, hipStream_t stream) {
-    constexpr int S = PA_DECODE_STAGES;
+    constexpr int S = stages_for<KV, D, BS>();
     constexpr int W = waves_for<KV, D, BS, S>();
     switch (group) {
         case 1: return launch_partition<KV, Q, D, BS, 1, W, S>(a, stream);

@@ -28,8 +28,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attn: effective KV GB/s (% of HBM peak), µs/step, seqs/s"
-KERNEL_SOURCES = ["paged_kv_cache_142_amd/csrc/pa_decode_kernel.hpp", "paged_kv_cache_142_amd/csrc/pa_common.hpp",
-                  "paged_kv_cache_142_amd/csrc/pa_decode_bf16.hip", "paged_kv_cache_142_amd/csrc/pa_decode_api.hip"]
+KERNEL_SOURCES = ["paged_kv_cache_142_amd/csrc/pa_decode_kernel.hpp", "paged_kv_cache_142_amd/csrc/pa_decode_gqa.hpp",
+                  "paged_kv_cache_142_amd/csrc/pa_common.hpp", "paged_kv_cache_142_amd/csrc/pa_decode_bf16.hip",
+                  "paged_kv_cache_142_amd/csrc/pa_decode_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_gqa_traffic.json")
 
 
@@ -43,6 +44,8 @@ def _parse():
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
+    p.add_argument("--graph", action="store_true",
+                   help="replay the step as a captured HIP graph (the four launches) instead of eager calls")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="instead of the benchmark, run a plain device copy of this many MiB per step "
                         "(reference for scaling the FETCH_SIZE/WRITE_SIZE counters)")
@@ -123,16 +126,37 @@ class Device:
                           block_tables=self.tables, seq_lens=self.lens, max_seq_len=wl.max_seq_len,
                           scale=float(wl.scale), partition_size=wl.partition_size, workspace=self.ws,
                           k_scale=self.k_scale, v_scale=self.v_scale, kv_dtype=kv)
+        self.dargs = dargs
         # identical calls every step: marshal the C arguments once
-        self.calls = [
+        self.calls = self._make_calls()
+        torch.cuda.synchronize()
+
+    def _make_calls(self):
+        pa, kv = self.pa, self.kv
+        return [
             pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, self.k_cache, self.v_cache,
                         self.step_slots, kv_dtype=kv),
             pa.prepared("pa_copy_blocks", self.k_cache, self.v_cache, self.pairs, kv_dtype=kv)
             if self.pairs.numel() else (lambda: None),
-            pa.prepared("pa_decode_partition", **dargs),
-            pa.prepared("pa_decode_reduce", **dargs),
+            pa.prepared("pa_decode_partition", **self.dargs),
+            pa.prepared("pa_decode_reduce", **self.dargs),
         ]
+
+    def capture(self):
+        """Capture one step (four launches, no memsets) into a HIP graph."""
+        import torch
+        pa, wl = self.pa, self.wl
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                calls = self._make_calls()
+                for call in calls:
+                    call()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        return g
 
     def step(self, ev=None):
         if ev is None:
@@ -219,22 +243,34 @@ def main():
         return
     wl = _workload(args.config, args.seed, args.partition_size)
     dev = Device(wl)
-    for _ in range(args.warmup):
+    graph = None
+    if args.graph:  # one eager step first (one-time kernel attribute setup), then capture
         dev.step()
+        torch.cuda.synchronize()
+        graph = dev.capture()
+    run = graph.replay if graph is not None else dev.step
+    for _ in range(args.warmup):
+        run()
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: exactly K steps, no markers between the launches
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for k in range(args.steps):
-        dev.step(evs[k])
+    for _ in range(args.steps):
+        run()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
     ms_per_step = gpu_ms / args.steps
+
+    # per-kernel durations: the same steps, eager, with an event around each launch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        dev.step(evs[k])
+    torch.cuda.synchronize()
 
     def avg(a, b):
         return float(np.mean([e[a].elapsed_time(e[b]) for e in evs])) * 1e3  # us
@@ -266,7 +302,8 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
         "decode_partition_us_p10_p90": [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
-        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        "step_mode": "hip_graph" if graph is not None else "eager",
+        "roofline": {"kernel": "pa_decode_partition launch (decode_plan_kernel + decode partition kernel)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }

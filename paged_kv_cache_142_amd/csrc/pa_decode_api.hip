@@ -13,15 +13,89 @@ static int num_partitions(int max_seq_len, int partition_size) {
     return (max_seq_len + partition_size - 1) / partition_size;
 }
 
-// Workspace: m[N][H][P_max] | l[N][H][P_max] | acc[N][H][P_max][D], float32,
-// each array starting on a 256-byte boundary.
-static size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int max_parts) {
+// Workspace: m[N][H][P_max] | l[N][H][P_max] | acc[N][H][P_max][D] (float32)
+// | plan (int32: count, then N * P_max work items), each part starting on a
+// 256-byte boundary.
+static size_t plan_offset(int num_seqs, int num_heads, int head_dim, int max_parts) {
     const size_t rows = (size_t)num_seqs * num_heads * max_parts;
-    return 2 * align256(rows * 4) + rows * head_dim * 4;
+    return 2 * align256(rows * 4) + align256(rows * head_dim * 4);
+}
+static size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int max_parts) {
+    return plan_offset(num_seqs, num_heads, head_dim, max_parts) +
+           4 * (PLAN_ITEMS_OFFSET + (size_t)num_seqs * max_parts);
+}
+
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_BUCKETS = 1024;
+
+// Work order for the partition kernel: every (sequence, partition) item,
+// largest first.  Workgroups are dispatched in index order, so giving the
+// low indices to the full partitions and the high ones to the short
+// remainders keeps the last workgroups short (largest-processing-time-first
+// list scheduling).  One workgroup; a counting sort on the partition's size in
+// blocks (sizes beyond PLAN_BUCKETS share the last bucket).  The order inside a
+// bucket may vary between calls; the results do not, since every item is
+// computed the same way whichever workgroup takes it.
+__global__ void __launch_bounds__(PLAN_THREADS) decode_plan_kernel(const DecodeArgs a) {
+    __shared__ int hist[PLAN_BUCKETS];
+    __shared__ int scan[PLAN_BUCKETS];
+    const int tid = threadIdx.x;
+    const int B = a.block_size;
+    const int P = a.partition_size;
+    const int PB = P / B;  // blocks of a full partition
+    const int NBK = min(PB, PLAN_BUCKETS);
+    auto bucket = [&](int size) { return min(PB - size, NBK - 1); };  // 0 = full partitions
+    for (int k = tid; k < PLAN_BUCKETS; k += PLAN_THREADS) hist[k] = 0;
+    __syncthreads();
+    for (int i = tid; i < a.num_seqs; i += PLAN_THREADS) {
+        const int T = a.seq_lens[i];
+        if (T <= 0 || T > a.max_seq_len || (T + B - 1) / B > a.max_blocks_per_seq) continue;
+        const int np = (T + P - 1) / P;
+        const int last = (T + B - 1) / B - (np - 1) * PB;
+        if (np > 1) atomicAdd(&hist[0], np - 1);
+        atomicAdd(&hist[bucket(last)], 1);
+    }
+    __syncthreads();
+    if (tid < NBK) scan[tid] = hist[tid];
+    __syncthreads();
+    for (int off = 1; off < NBK; off <<= 1) {  // inclusive scan
+        const int v = (tid < NBK && tid >= off) ? scan[tid - off] : 0;
+        __syncthreads();
+        if (tid < NBK) scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < NBK) hist[tid] = scan[tid] - hist[tid];  // first slot of each bucket
+    if (tid == 0) a.plan[0] = scan[NBK - 1];
+    __syncthreads();
+    for (int i = tid; i < a.num_seqs; i += PLAN_THREADS) {
+        const int T = a.seq_lens[i];
+        if (T <= 0 || T > a.max_seq_len || (T + B - 1) / B > a.max_blocks_per_seq) continue;
+        const int np = (T + P - 1) / P;
+        const int last = (T + B - 1) / B - (np - 1) * PB;
+        for (int p = 0; p < np; ++p) {
+            const int pos = atomicAdd(&hist[bucket(p < np - 1 ? PB : last)], 1);
+            a.plan[PLAN_ITEMS_OFFSET + pos] = i * a.max_partitions + p;
+        }
+    }
+}
+
+// Wave-wide max and sum (every lane receives the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
 }
 
 // Merge the partition states of one (sequence, query head); one thread per
-// output element.  Partitions are visited in index order, so the result is
+// output element, D threads.  Partition states are fetched 64 at a time with
+// one vector load (lane p holds partition p), merged across the wave, and
+// the per-partition weights broadcast with readlane; groups of 64 are folded
+// with the same log-sum-exp rule in index order, so the result is
 // deterministic.  Also writes the rows the partition kernel does not: empty
 // sequences (zeros) and invalid ones (NaN).
 template <int D>
@@ -29,6 +103,7 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(const DecodeArgs a) {
     const int seq = blockIdx.x / a.num_heads;
     const int hq = blockIdx.x - seq * a.num_heads;
     const int d = threadIdx.x;
+    const int lane = d & 63;
     const int T = a.seq_lens[seq];
     const size_t row = (size_t)seq * a.num_heads + hq;
     float o;
@@ -40,13 +115,27 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(const DecodeArgs a) {
         const int n_parts = (T + a.partition_size - 1) / a.partition_size;
         if (n_parts == 1) return;  // finished by the partition kernel
         const size_t base = row * a.max_partitions;
-        float M = -INFINITY;
-        for (int p = 0; p < n_parts; ++p) M = fmaxf(M, a.part_m[base + p]);
-        float L = 0.f, A = 0.f;
-        for (int p = 0; p < n_parts; ++p) {
-            const float f = fast_exp2(a.part_m[base + p] - M);
-            L = fmaf(f, a.part_l[base + p], L);
-            A = fmaf(f, a.part_acc[(base + p) * D + d], A);
+        float M = -INFINITY, L = 0.f, A = 0.f;
+        for (int p0 = 0; p0 < n_parts; p0 += 64) {
+            const int np = min(64, n_parts - p0);
+            const bool have = lane < np;
+            const float mp = have ? a.part_m[base + p0 + lane] : -INFINITY;
+            const float lp = have ? a.part_l[base + p0 + lane] : 0.f;
+            const float Mg = wave_max(mp);  // finite: every partition holds tokens
+            const float Mn = fmaxf(M, Mg);
+            const float wp = have ? fast_exp2(mp - Mn) : 0.f;
+            const float Lg = wave_sum(wp * lp);
+            const float f = fast_exp2(M - Mn);  // 0 on the first group (M = -inf)
+            float Ag = 0.f;
+            const float* accp = a.part_acc + (base + p0) * D + d;
+#pragma unroll 8
+            for (int p = 0; p < np; ++p) {
+                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), p));
+                Ag = fmaf(w, accp[(size_t)p * D], Ag);
+            }
+            L = L * f + Lg;
+            A = A * f + Ag;
+            M = Mn;
         }
         o = A / L;
     }
@@ -92,6 +181,8 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     const int max_parts = num_partitions(max_seq_len, partition_size);
     if (max_parts > 65535) return PA_ERR_SHAPE;
     if ((long long)num_seqs * num_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    // partition grid: one workgroup per (item, kv head), at most 512 threads each
+    if ((long long)num_seqs * max_parts * num_kv_heads * 512 > 0xffffffffLL) return PA_ERR_SHAPE;
     pr.nothing_to_do = num_seqs == 0;
     if (pr.nothing_to_do) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
@@ -126,6 +217,7 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.part_m = (float*)workspace;
     a.part_l = (float*)((char*)workspace + align256(rows * 4));
     a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
+    a.plan = (int*)((char*)workspace + plan_offset(num_seqs, num_heads, head_dim, max_parts));
     pr.head_dim = head_dim;
     pr.group = group;
     pr.kv_dtype = kv_dtype;
@@ -135,6 +227,8 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
 
 static int run_partition(const Prepared& pr, hipStream_t stream) {
     if (pr.args.max_partitions == 0) return PA_OK;  // every sequence is empty
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pr.args);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     switch (pr.kv_dtype) {
         case PA_DTYPE_F32: return launch_partition_f32(pr.args, pr.head_dim, pr.group, stream);
         case PA_DTYPE_F16: return launch_partition_f16(pr.args, pr.head_dim, pr.group, stream);

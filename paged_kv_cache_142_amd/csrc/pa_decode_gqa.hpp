@@ -54,7 +54,8 @@ struct GqaShape {
     static constexpr int R = 64 / NG;        // value-layout token rows per pass
     static constexpr int VPASS = 16 / R;
     static constexpr int SCRATCH = 512;      // p[16][G] + alpha[G], padded
-    static constexpr int RING = S * STAGE + SCRATCH;
+    static constexpr int QBYTES = G * D * 2; // the group's query rows
+    static constexpr int RING = S * STAGE + SCRATCH + QBYTES;
     static constexpr int MERGE_HEAD = ((2 * W * G + W) * 4 + 15) / 16 * 16;
     static constexpr int MERGE = MERGE_HEAD + W * R * G * D * 4;
     static constexpr int LDS = (W * RING > MERGE) ? W * RING : MERGE;
@@ -78,8 +79,13 @@ __device__ __forceinline__ float dpp_max(float x) {
     return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true)));
 }
 
+#ifndef PA_GQA_WAVES_PER_SIMD
+#define PA_GQA_WAVES_PER_SIMD 3
+#endif
+
+// At least PA_GQA_WAVES_PER_SIMD waves per SIMD: caps registers at 168.
 template <Fmt KV, int D, int BS, int W, int S>
-__global__ void __launch_bounds__(W * 64)
+__global__ void __launch_bounds__(W * 64, PA_GQA_WAVES_PER_SIMD)
 decode_partition_gqa4_kernel(const DecodeArgs a) {
     using Sh = GqaShape<KV, D, BS, W, S>;
     using Row = LaneRow<KV, D>;
@@ -96,40 +102,32 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     const int r = lane / NG;
     const int c = lane % NG;
 
-    const int seq = blockIdx.x / a.num_kv_heads;
-    const int kvh = blockIdx.x - seq * a.num_kv_heads;
-    const int part = blockIdx.y;
+    int seq, kvh, part;
+    if (!partition_work_item(a, seq, kvh, part)) return;
+    const int P = a.partition_size;
+    const int lb0 = part * P / BS;  // first logical block of the partition
+    // Block ids of the whole partition, fetched together with the sequence
+    // length (one lane per block, up to 64).  The read is in bounds of the
+    // table row: part < ceil(max_seq_len / P), so lb0 < max_blocks_per_seq;
+    // entries past the sequence's last block are loaded but never used.
+    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0;
+    const int id_lim = min(min(P / BS, 64), a.max_blocks_per_seq - lb0);
+    int ids = lane < id_lim ? bt[lane] : 0;
     const int T = a.seq_lens[seq];
+    // wait for the ids here, together with the length: the compiler does not
+    // see the asynchronous copies below and would otherwise wait for them too
+    asm volatile("" : "+v"(ids));
     if (T <= 0 || T > a.max_seq_len) return;
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
-    const int P = a.partition_size;
     const int n_parts = (T + P - 1) / P;
     if (part >= n_parts) return;
     const int tok0 = part * P;
     const int tok1 = min(tok0 + P, T);
-    const int lb0 = tok0 / BS;
     const int nblk = (tok1 - tok0 + BS - 1) / BS;
     // this wave's blocks: a contiguous, balanced share of the partition
     const int kb0 = nblk * wave / W;
     const int nbw = nblk * (wave + 1) / W - kb0;
-    const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0 + kb0;
-    // physical ids of the wave's blocks, one per lane (64 at a time); read
-    // with readlane when a block's copy is issued
-    int ids = lane < nbw ? bt[lane] : 0;
     const int hq0 = kvh * G;
-
-    // Query words of this lane's head and half row.
-    uint32_t qw[Sh::QW];
-    {
-        const char* qrow = (const char*)a.q + (((size_t)seq * a.num_heads + hq0 + hl) * D + half * (D / 2)) * 2;
-#pragma unroll
-        for (int i = 0; i < Sh::HALF_G; ++i) {
-            const u32x4 v = *(const u32x4*)(qrow + i * 16);
-            qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
-        }
-#pragma unroll
-        for (int i = 0; i < Sh::QW; ++i) asm volatile("" : "+v"(qw[i]));
-    }
     const float qk_scale = a.qk_scale_log2;
 
     // Source offset of this lane's 16 bytes in each 1 KiB copy of a K tile
@@ -148,12 +146,28 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     char* ring = smem + wave * Sh::RING;
     float* p_lds = (float*)(ring + S * Sh::STAGE);  // [16][G]
     float* alpha_lds = p_lds + 16 * G;                   // [G]
+    const char* q_lds = ring + S * Sh::STAGE + Sh::SCRATCH;  // [G][D] query elements
     const uint32_t ring_lds = lds_addr_of(smem) + (uint32_t)(wave * Sh::RING);
     int invalid = 0;
 
+    // The group's query rows go to LDS with the same asynchronous copies, ahead
+    // of the first block; they are read into registers once that block landed.
+    if (nbw > 0 && lane * 16 < Sh::QBYTES)
+        dma16_to_lds((const char*)a.q + ((size_t)seq * a.num_heads + hq0) * D * 2 + lane * 16,
+                     ring_lds + (uint32_t)(S * Sh::STAGE + Sh::SCRATCH));
+    uint32_t qw[Sh::QW];
+    auto load_q = [&]() {
+        const char* qrow = q_lds + (hl * D + half * (D / 2)) * 2;
+#pragma unroll
+        for (int i = 0; i < Sh::HALF_G; ++i) {
+            const u32x4 v = *(const u32x4*)(qrow + i * 16);
+            qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
+        }
+    };
+
     auto issue = [&](int k, int stage) {
-        if (k > 0 && (k & 63) == 0) ids = k + lane < nbw ? bt[k + lane] : 0;
-        int pb = __builtin_amdgcn_readlane(ids, k & 63);
+        const int idx = kb0 + k;  // block index inside the partition
+        int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : bt[idx];
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
@@ -259,6 +273,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     for (int k = 0; k < nbw; ++k) {
         if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
         wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
+        if (k == 0) load_q();
         const char* sp = ring + stage * Sh::STAGE;
         const int blk_tok0 = (lb0 + kb0 + k) * BS;
         if (blk_tok0 + BS <= T) {
@@ -327,7 +342,7 @@ int launch_partition_gqa4(const DecodeArgs& a, hipStream_t stream) {
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.max_partitions);
+    const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

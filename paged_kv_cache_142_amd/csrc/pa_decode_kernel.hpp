@@ -63,7 +63,26 @@ struct DecodeArgs {
     float* part_m;    // [num_seqs][num_heads][max_partitions]
     float* part_l;    // [num_seqs][num_heads][max_partitions]
     float* part_acc;  // [num_seqs][num_heads][max_partitions][head_dim]
+    // Work order written by the plan kernel: plan[0] = number of (sequence,
+    // partition) items, plan[PLAN_ITEMS_OFFSET + k] = seq * max_partitions +
+    // partition of the k-th item, largest first.
+    int* plan;
 };
+
+constexpr int PLAN_ITEMS_OFFSET = 64;
+
+// The (sequence, kv head, partition) of this partition workgroup: workgroup
+// x = item * num_kv_heads + kv head, items in the plan's order.  Returns
+// false for workgroups past the last item.
+__device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, int& seq, int& kvh, int& part) {
+    const int item = blockIdx.x / a.num_kv_heads;
+    kvh = blockIdx.x - item * a.num_kv_heads;
+    if (item >= a.plan[0]) return false;
+    const int code = a.plan[PLAN_ITEMS_OFFSET + item];
+    seq = code / a.max_partitions;
+    part = code - seq * a.max_partitions;
+    return true;
+}
 
 __device__ __forceinline__ void store_out(void* out, int dtype, size_t idx, float v) {
     if (dtype == PA_DTYPE_F32)
@@ -290,9 +309,8 @@ decode_partition_kernel(const DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane / LPR;
     const int c = lane % LPR;
-    const int seq = blockIdx.x / a.num_kv_heads;
-    const int kvh = blockIdx.x - seq * a.num_kv_heads;
-    const int part = blockIdx.y;
+    int seq, kvh, part;
+    if (!partition_work_item(a, seq, kvh, part)) return;
 
     const int T = a.seq_lens[seq];
     if (T <= 0 || T > a.max_seq_len) return;  // empty or invalid rows: written by the reduce kernel
@@ -522,7 +540,7 @@ int launch_partition(const DecodeArgs& a, hipStream_t stream) {
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads), (unsigned)a.max_partitions);
+    const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -42,13 +42,14 @@ def test_status_strings(lib):
 
 
 def test_workspace_size_formula(lib):
-    # m and l arrays each padded to 256 bytes, then acc[N][H][P][D] float32
+    # m, l, acc[N][H][P][D] float32 arrays, each padded to 256 bytes, then the
+    # work plan: 64 header ints and one int per (sequence, partition)
     n, h, d, msl, p = 64, 32, 128, 4096, 512
     parts = 8
     rows = n * h * parts
     pad = lambda x: (x + 255) // 256 * 256
-    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == 2 * pad(rows * 4) + rows * d * 4
-    assert lib.pa_decode_workspace_size(1, 1, 64, 0, 16) == 0
+    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == 2 * pad(rows * 4) + pad(rows * d * 4) + 4 * (64 + n * parts)
+    assert lib.pa_decode_workspace_size(1, 1, 64, 0, 16) == 4 * 64
     assert lib.pa_decode_workspace_size(-1, 1, 64, 10, 16) == 0
     assert lib.pa_decode_workspace_size(1, 1, 64, 10, 0) == 0
 

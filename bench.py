@@ -81,7 +81,8 @@ def _describe(wl):
     return (f"{wl.name}: {wl.num_seqs} seqs, sum T={int(wl.seq_lens.sum())} (max {wl.max_seq_len}), "
             f"{wl.num_heads}/{wl.num_kv_heads} heads, d={wl.head_dim}, B={wl.block_size}, {wl.kv_dtype} KV, "
             f"{wl.q_dtype} q, f32 out and accumulation, P={wl.partition_size}; step = scatter of "
-            f"{wl.num_seqs} new tokens + copy of {len(wl.copy_pairs)} blocks + split-KV decode")
+            f"{wl.num_seqs} new tokens{' (bf16, quantized on write)' if wl.step_keys_src is not None else ''}"
+            f" + copy of {len(wl.copy_pairs)} blocks + split-KV decode")
 
 
 class Device:
@@ -108,8 +109,14 @@ class Device:
         kv = "fp8_e4m3" if self.fp8 else None
         pa.pa_reshape_and_cache(keys[pre].contiguous(), values[pre].contiguous(), self.k_cache, self.v_cache,
                                 slots[pre].contiguous(), kv_dtype=kv)
-        self.step_keys = keys[step].contiguous()
-        self.step_values = values[step].contiguous()
+        # fp8 pools: the step's new tokens arrive in bf16 and are quantized on write
+        self.quantize_step = wl.step_keys_src is not None
+        if self.quantize_step:
+            self.step_keys = up(wl.step_keys_src, "bf16")
+            self.step_values = up(wl.step_values_src, "bf16")
+        else:
+            self.step_keys = keys[step].contiguous()
+            self.step_values = values[step].contiguous()
         self.step_slots = slots[step].contiguous()
         del keys, values
         self.pairs = torch.from_numpy(wl.copy_pairs).to(dev)
@@ -133,9 +140,13 @@ class Device:
 
     def _make_calls(self):
         pa, kv = self.pa, self.kv
+        scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, self.k_cache,
+                               self.v_cache, self.k_scale, self.v_scale, self.step_slots)
+                   if self.quantize_step else
+                   pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, self.k_cache, self.v_cache,
+                               self.step_slots, kv_dtype=kv))
         return [
-            pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, self.k_cache, self.v_cache,
-                        self.step_slots, kv_dtype=kv),
+            scatter,
             pa.prepared("pa_copy_blocks", self.k_cache, self.v_cache, self.pairs, kv_dtype=kv)
             if self.pairs.numel() else (lambda: None),
             pa.prepared("pa_decode_partition", **self.dargs),

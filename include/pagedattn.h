@@ -96,6 +96,31 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          void* stream);
 
 /*
+ * pa_reshape_and_cache_fp8 -- store new tokens into FP8 pools, quantizing.
+ *
+ * The same scatter as pa_reshape_and_cache, for pools in PA_DTYPE_FP8_E4M3
+ * (one byte per element with a float32 scale per kv head; youngju.dev, same
+ * page, section "KV量子化: FP8とINT8"), from new K/V rows in a wider format.
+ * For every element x of key[t][h][:] (value[t][h][:] likewise):
+ *     code = E4M3FN(x / k_scale[h])   (v_scale[h] for values)
+ * where x is widened exactly to float32, the quotient is the IEEE float32
+ * division (round to nearest even), a NaN quotient gives code 0x7F, and
+ * magnitudes beyond 448 (infinities included) saturate to 448 before the
+ * conversion rounds to the nearest code (ties to even).  The stored value
+ * code * scale then reads back through pa_decode's FP8 path.
+ *   key, value   [num_tokens][num_kv_heads][head_dim] in src_dtype (F32, F16
+ *                or BF16), 16-byte aligned
+ *   k_cache, v_cache   FP8 pools [num_blocks][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale   [num_kv_heads] float32, device
+ *   slot_mapping, num_tokens, shapes: as for pa_reshape_and_cache (slots < 0
+ *                or past the pool are skipped).
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, int src_dtype, void* k_cache,
+                             void* v_cache, const float* k_scale, const float* v_scale,
+                             const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, void* stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks for copy-on-write.
  *
  * When a sequence must write into a block whose reference count exceeds one,

@@ -45,5 +45,5 @@ from .attention import (  # noqa: F401
     paged_decode_row,
     split_kv_attention,
 )
-from .formats import decode_elements, e4m3fn_table  # noqa: F401
-from .paging import copy_blocks, gather_sequence, reshape_and_cache  # noqa: F401
+from .formats import decode_elements, e4m3fn_encode, e4m3fn_table, quantize_to_e4m3fn  # noqa: F401
+from .paging import copy_blocks, gather_sequence, quantize_reshape_and_cache, reshape_and_cache  # noqa: F401

@@ -72,6 +72,50 @@ def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
+def e4m3fn_encode(x) -> np.ndarray:
+    """E4M3FN codes of float values: nearest code, ties to the even code,
+    saturated at +-448; NaN gives 0x7F.
+
+    The nearest code is found by comparing against every finite code value
+    (exact in float64).  On a tie the even code wins, which is the code whose
+    mantissa field is even (round to nearest even).  Values beyond the
+    largest finite magnitude, infinities included, become +-448, the
+    saturating reading of storing a value too large for the format.
+
+    Parity: pinned against torch's float8_e4m3fn conversion on every
+    bfloat16 value inside the format's range and on dense float32 samples,
+    and against hand-picked ties, subnormals and overflow cases.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.array([c for c in range(256) if not np.isnan(_E4M3FN[c])], dtype=np.int64)
+    values = _E4M3FN[finite]
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat = x.reshape(-1)
+    res = out.reshape(-1)
+    for n, v in enumerate(flat):
+        if np.isnan(v):
+            res[n] = 0x7F
+            continue
+        v = min(max(v, -448.0), 448.0)
+        dist = np.abs(values - v)
+        best = np.flatnonzero(dist == dist.min())
+        codes = finite[best]
+        if len(codes) > 1:  # tie between two neighbours (or +0/-0)
+            same_sign = codes[(codes >= 0x80) == bool(np.signbit(v))]
+            codes = same_sign if len(same_sign) else codes
+            even = codes[(codes & 1) == 0]
+            codes = even if len(even) else codes
+        res[n] = codes[0]
+    return out
+
+
+def quantize_to_e4m3fn(x32, scale32) -> np.ndarray:
+    """Codes of ``x / scale``: the quotient is the IEEE float32 division of
+    the float32 value by the float32 scale, then ``e4m3fn_encode``."""
+    q = np.asarray(x32, dtype=np.float32) / np.asarray(scale32, dtype=np.float32)
+    return e4m3fn_encode(q.astype(np.float32))
+
+
 def decode_elements(raw: np.ndarray, dtype: str) -> np.ndarray:
     """Float64 values of stored elements of format ``dtype`` (no scale)."""
     if dtype == "f32":

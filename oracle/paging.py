@@ -88,3 +88,25 @@ def gather_sequence(cache, table_row, seq_len, block_size):
         return np.zeros((h, 0, d), dtype=cache.dtype)
     rows = np.concatenate(tiles, axis=1)  # [H_kv][num_logical*B][d]
     return rows[:, : int(seq_len), :]
+
+
+def quantize_reshape_and_cache(k_cache, v_cache, key32, value32, k_scale, v_scale, slot_mapping, block_size):
+    """Quantize float32 K/V rows to E4M3FN codes and scatter them, in place.
+
+    ``key32``/``value32``: ``[num_tokens][H_kv][d]`` float32 values (the new
+    tokens' K and V widened exactly from their stored format); head ``h`` is
+    divided by ``k_scale[h]`` (``v_scale[h]``) in float32 and encoded with
+    ``formats.e4m3fn_encode``.  FP8 KV storage with a scale: youngju.dev,
+    "KVキャッシュとPagedAttention — 推論メモリのすべて", section "KV量子化:
+    FP8とINT8".
+
+    Parity: the encoder is pinned in the oracle tests; the scatter is the
+    pinned ``reshape_and_cache``.
+    """
+    from .formats import quantize_to_e4m3fn
+    key32 = np.asarray(key32, dtype=np.float32)
+    value32 = np.asarray(value32, dtype=np.float32)
+    kcodes = np.stack([quantize_to_e4m3fn(key32[:, h], np.float32(k_scale[h])) for h in range(key32.shape[1])], axis=1)
+    vcodes = np.stack([quantize_to_e4m3fn(value32[:, h], np.float32(v_scale[h])) for h in range(value32.shape[1])],
+                      axis=1)
+    reshape_and_cache(k_cache, v_cache, kcodes, vcodes, slot_mapping, block_size)

@@ -70,6 +70,17 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, kv_dtype=No
         _stream(stream, k_cache.device)), "pa_reshape_and_cache")
 
 
+def pa_reshape_and_cache_fp8(key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping, src_dtype=None,
+                             stream=None):
+    """Quantize ``key``/``value`` (fp32/fp16/bf16) to E4M3 codes with per-head
+    scales and scatter them into the fp8 pools at ``slot_mapping``."""
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    _check(_lib.load().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), dtype_code(key, src_dtype), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), int(slot_mapping.numel()), num_kv_heads, head_dim, block_size,
+        num_blocks, _stream(stream, k_cache.device)), "pa_reshape_and_cache_fp8")
+
+
 def pa_copy_blocks(k_cache, v_cache, block_pairs, kv_dtype=None, stream=None):
     """Copy whole blocks for each ``(src, dst)`` row of ``block_pairs`` (int64, device)."""
     num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
@@ -110,6 +121,12 @@ def prepared(name, *args, **kw):
         nb, hkv, bs, d = k_cache.shape
         argv = (_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), int(slot_mapping.numel()),
                 hkv, d, bs, nb, dtype_code(k_cache, kw.get("kv_dtype")), _stream(kw.get("stream"), k_cache.device))
+    elif name == "pa_reshape_and_cache_fp8":
+        key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping = args
+        nb, hkv, bs, d = k_cache.shape
+        argv = (_ptr(key), _ptr(value), dtype_code(key, kw.get("src_dtype")), _ptr(k_cache), _ptr(v_cache),
+                _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping), int(slot_mapping.numel()), hkv, d, bs, nb,
+                _stream(kw.get("stream"), k_cache.device))
     elif name == "pa_copy_blocks":
         k_cache, v_cache, block_pairs = args
         nb, hkv, bs, d = k_cache.shape

@@ -21,6 +21,8 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_c_int]),
     "pa_reshape_and_cache": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_int, _vp]),
+    "pa_reshape_and_cache_fp8": (_c_int, [_vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, _vp]),
     "pa_copy_blocks": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "pa_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pa_decode": (_c_int, _DECODE_ARGS),

@@ -56,6 +56,75 @@ copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
     cache[dst * granules_per_block + g] = cache[src * granules_per_block + g];
 }
 
+// Quantize-on-write: one thread per 16 output codes (16 elements of one
+// token row of one head).  code = E4M3FN(x / scale[h]): the quotient is the
+// IEEE float32 division, NaN stays NaN (code 0x7F), and magnitudes beyond
+// 448 saturate to 448 before the round-to-nearest-even conversion.
+template <Fmt SRC>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_fp8_kernel(const char* __restrict__ key, const char* __restrict__ value,
+                             uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                             const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+                             const int64_t* __restrict__ slot_mapping, int64_t total, int groups_per_row,
+                             int num_kv_heads, int block_size, int head_dim, int64_t num_slots) {
+    constexpr int SB = FmtBytes<SRC>::value;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int per_token = 2 * num_kv_heads * groups_per_row;
+    const int64_t t = idx / per_token;
+    const int rem = (int)(idx - t * per_token);
+    const int which = rem / (num_kv_heads * groups_per_row);
+    const int hg = rem - which * num_kv_heads * groups_per_row;
+    const int h = hg / groups_per_row;
+    const int g = hg - h * groups_per_row;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t block = slot / block_size;
+    const int64_t row = slot - block * block_size;
+    const char* src = (which == 0 ? key : value) + ((t * num_kv_heads + h) * head_dim + g * 16) * SB;
+    const float scale = (which == 0 ? k_scale : v_scale)[h];
+    float x[16];
+    if constexpr (SRC == Fmt::F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = ((const float4*)src)[i];
+            x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = ((const u32x4*)src)[i];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                x[8 * i + 2 * p] = SRC == Fmt::BF16 ? bf16_lo(w[p]) : f16_lo(w[p]);
+                x[8 * i + 2 * p + 1] = SRC == Fmt::BF16 ? bf16_hi(w[p]) : f16_hi(w[p]);
+            }
+        }
+    }
+    uint32_t packed[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float q[4];
+        bool nan[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = __fdiv_rn(x[4 * i + j], scale);
+            nan[j] = v != v;
+            q[j] = nan[j] ? 0.f : fminf(fmaxf(v, -448.f), 448.f);
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+        uint32_t u = (uint32_t)w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (nan[j]) u = (u & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
+        packed[i] = u;
+    }
+    uint8_t* dst = (which == 0 ? k_cache : v_cache) + ((block * num_kv_heads + h) * block_size + row) * head_dim + g * 16;
+    *(u32x4*)dst = u32x4{packed[0], packed[1], packed[2], packed[3]};
+}
+
 static bool valid_kv_dtype(int d) { return d >= PA_DTYPE_F32 && d <= PA_DTYPE_FP8_E4M3; }
 static bool supported_dim(int d) { return d == 64 || d == 128; }
 static bool supported_block(int b) { return b == 16 || b == 32; }
@@ -94,6 +163,40 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
                        (hipStream_t)stream, (const u32x4*)key, (const u32x4*)value,
                        (u32x4*)k_cache, (u32x4*)v_cache, slot_mapping, total, granules_per_row,
                        num_kv_heads, block_size, (int64_t)num_blocks * block_size);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, int src_dtype,
+                                        void* k_cache, void* v_cache, const float* k_scale,
+                                        const float* v_scale, const int64_t* slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int num_blocks, void* stream) {
+    using namespace pa;
+    if (src_dtype != PA_DTYPE_F32 && src_dtype != PA_DTYPE_F16 && src_dtype != PA_DTYPE_BF16)
+        return PA_ERR_DTYPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+        return PA_ERR_SHAPE;
+    if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !k_scale || !v_scale || !slot_mapping) return PA_ERR_NULL;
+    const int groups_per_row = head_dim / 16;
+    const int64_t total = (int64_t)num_tokens * 2 * num_kv_heads * groups_per_row;
+    const int64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const int64_t slots = (int64_t)num_blocks * block_size;
+    const hipStream_t s = (hipStream_t)stream;
+#define PA_LAUNCH_Q(F)                                                                          \
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<F>, dim3((unsigned)grid), dim3(256), 0, s, \
+                       (const char*)key, (const char*)value, (uint8_t*)k_cache, (uint8_t*)v_cache,  \
+                       k_scale, v_scale, slot_mapping, total, groups_per_row, num_kv_heads,     \
+                       block_size, head_dim, slots)
+    if (src_dtype == PA_DTYPE_BF16)
+        PA_LAUNCH_Q(Fmt::BF16);
+    else if (src_dtype == PA_DTYPE_F16)
+        PA_LAUNCH_Q(Fmt::F16);
+    else
+        PA_LAUNCH_Q(Fmt::F32);
+#undef PA_LAUNCH_Q
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

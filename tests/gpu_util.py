@@ -65,8 +65,13 @@ class DeviceCase:
         self.v_scale = torch.from_numpy(wl.v_scale).to(DEV) if wl.v_scale is not None else None
         self.out_fmt = out_fmt
         self.out = poison_device((wl.num_seqs, wl.num_heads, wl.head_dim), out_fmt)
-        self.step_keys = self.keys.index_select(0, self.step).contiguous()
-        self.step_values = self.values.index_select(0, self.step).contiguous()
+        self.quantize_step = wl.step_keys_src is not None
+        if self.quantize_step:  # the step's tokens arrive in bf16 and are quantized on write
+            self.step_keys = to_device(wl.step_keys_src, "bf16")
+            self.step_values = to_device(wl.step_values_src, "bf16")
+        else:
+            self.step_keys = self.keys.index_select(0, self.step).contiguous()
+            self.step_values = self.values.index_select(0, self.step).contiguous()
         self.step_slots = self.slots.index_select(0, self.step).contiguous()
         self.partition_size = wl.partition_size
         self.ws = None
@@ -84,7 +89,11 @@ class DeviceCase:
         self.partition_size = partition_size
 
     def run_cache_ops(self):
-        pa.pa_reshape_and_cache(self.step_keys, self.step_values, self.k_cache, self.v_cache, self.step_slots)
+        if self.quantize_step:
+            pa.pa_reshape_and_cache_fp8(self.step_keys, self.step_values, self.k_cache, self.v_cache, self.k_scale,
+                                        self.v_scale, self.step_slots)
+        else:
+            pa.pa_reshape_and_cache(self.step_keys, self.step_values, self.k_cache, self.v_cache, self.step_slots)
         if len(self.wl.copy_pairs):
             pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs)
 
@@ -114,7 +123,12 @@ def oracle_pools(wl):
     pre = wl.prefill_rows()
     oracle.reshape_and_cache(kc, vc, wl.keys[pre], wl.values[pre], wl.slots[pre], wl.block_size)
     st = wl.step_rows()
-    oracle.reshape_and_cache(kc, vc, wl.keys[st], wl.values[st], wl.slots[st], wl.block_size)
+    if wl.step_keys_src is not None:
+        k32 = oracle.decode_elements(wl.step_keys_src, "bf16").astype(np.float32)
+        v32 = oracle.decode_elements(wl.step_values_src, "bf16").astype(np.float32)
+        oracle.quantize_reshape_and_cache(kc, vc, k32, v32, wl.k_scale, wl.v_scale, wl.slots[st], wl.block_size)
+    else:
+        oracle.reshape_and_cache(kc, vc, wl.keys[st], wl.values[st], wl.slots[st], wl.block_size)
     oracle.copy_blocks(kc, vc, wl.copy_pairs)
     return kc, vc
 

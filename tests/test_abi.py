@@ -20,7 +20,7 @@ FAKE = 4096  # a non-null, 16-byte aligned address that validation never reaches
 def _declared():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -72,6 +72,25 @@ def test_reshape_and_cache_validation(lib):
     assert _rc(lib, block=8) == UNSUP
     for ptr in ("key", "value", "k_cache", "v_cache", "slots"):
         assert _rc(lib, **{ptr: None}) == NULL
+
+
+def _rq(lib, **kw):
+    a = dict(key=FAKE, value=FAKE, src=BF16, k_cache=FAKE, v_cache=FAKE, ks=FAKE, vs=FAKE, slots=FAKE, n=4,
+             heads=8, dim=128, block=16, blocks=100)
+    a.update(kw)
+    return lib.pa_reshape_and_cache_fp8(a["key"], a["value"], a["src"], a["k_cache"], a["v_cache"], a["ks"],
+                                        a["vs"], a["slots"], a["n"], a["heads"], a["dim"], a["block"], a["blocks"],
+                                        None)
+
+
+def test_reshape_and_cache_fp8_validation(lib):
+    assert _rq(lib, n=0) == OK
+    assert _rq(lib, src=FP8) == DTYPE
+    assert _rq(lib, src=9) == DTYPE
+    assert _rq(lib, n=-1) == SHAPE
+    assert _rq(lib, dim=80) == UNSUP
+    for ptr in ("key", "value", "k_cache", "v_cache", "ks", "vs", "slots"):
+        assert _rq(lib, **{ptr: None}) == NULL
 
 
 def _cb(lib, **kw):

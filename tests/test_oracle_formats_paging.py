@@ -188,3 +188,50 @@ def test_package_exports():
     for name in ["dense_attention", "paged_decode", "online_softmax_attention", "split_kv_attention",
                  "lse_merge", "reshape_and_cache", "copy_blocks", "gather_sequence", "e4m3fn_table"]:
         assert callable(getattr(oracle, name))
+
+
+# --------------------------------------------------------- fp8 encoder
+
+
+def test_e4m3fn_encode_round_trips_every_finite_code():
+    t = formats.e4m3fn_table()
+    codes = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    assert np.array_equal(formats.e4m3fn_encode(t[codes]), codes)
+
+
+def test_e4m3fn_encode_matches_torch_on_all_bf16_values_in_range():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = formats.bf16_bits_to_f64(bits)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    vals = vals[keep]
+    ref = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(formats.e4m3fn_encode(vals), ref)
+
+
+def test_e4m3fn_encode_matches_torch_on_float32_samples():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.standard_normal(20000) * 50, rng.uniform(-448, 448, 5000),
+                        rng.standard_normal(5000) * 2.0 ** -8]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(formats.e4m3fn_encode(x.astype(np.float64)), ref)
+
+
+@pytest.mark.parametrize("value,code", [
+    (2.0 ** -10, 0x00),            # half the smallest subnormal: tie, even code 0
+    (1.5 * 2.0 ** -9, 0x02),       # tie between codes 1 and 2
+    (2.5 * 2.0 ** -9, 0x02),       # tie between codes 2 and 3
+    (1.0 + 2.0 ** -4, 0x38),       # tie between 1.0 (0x38) and 1.125 (0x39)
+    (1.0 + 3 * 2.0 ** -4, 0x3A),   # tie between 1.125 and 1.25: even 0x3A
+    (440.0, 0x7E), (449.0, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (np.inf, 0x7E),
+    (-464.0, 0xFE), (-np.inf, 0xFE), (-0.0, 0x80), (np.nan, 0x7F),
+])
+def test_e4m3fn_encode_hand_cases(value, code):
+    assert formats.e4m3fn_encode(np.array([value]))[0] == code
+
+
+def test_quantize_uses_float32_division():
+    x = np.array([1.0, 3.0, -7.5], np.float32)
+    s = np.float32(0.1)
+    want = formats.e4m3fn_encode((x / s).astype(np.float64))
+    assert np.array_equal(formats.quantize_to_e4m3fn(x, s), want)
+    assert formats.e4m3fn_table()[formats.quantize_to_e4m3fn(np.array([448 * 0.1], np.float32), s)[0]] == 448.0

@@ -142,6 +142,10 @@ class DecodeWorkload:
     k_scale: Optional[np.ndarray]  # float32 [H_kv] for fp8, else None
     v_scale: Optional[np.ndarray]
     copy_pairs: np.ndarray      # int64 [n][2]
+    # fp8 pools only: the step's new tokens as bf16 rows [N][H_kv][d] (raw
+    # bits), quantized on write instead of copied from keys/values
+    step_keys_src: Optional[np.ndarray] = None
+    step_values_src: Optional[np.ndarray] = None
 
     @property
     def max_blocks_per_seq(self):
@@ -216,7 +220,13 @@ def build_decode_workload(name, seed, *, seq_lens, num_heads, num_kv_heads, head
     src = rng.choice(in_use, size=num_copy_pairs, replace=False) if num_copy_pairs else np.zeros(0, np.int64)
     dst = rng.choice(spare, size=num_copy_pairs, replace=False) if num_copy_pairs else np.zeros(0, np.int64)
     pairs = np.stack([src, dst], axis=1).astype(np.int64).reshape(-1, 2)
+    step_src = (None, None)
+    if kv_dtype == "fp8_e4m3":
+        n_step = int((seq_lens > 0).sum())
+        step_src = (_token_rows(_seed(seed, 6), n_step, num_kv_heads, head_dim, "bf16")[0],
+                    _token_rows(_seed(seed, 7), n_step, num_kv_heads, head_dim, "bf16")[0])
     return DecodeWorkload(
+        step_keys_src=step_src[0], step_values_src=step_src[1],
         name=name, seed=seed, kv_dtype=kv_dtype, q_dtype=q_dtype, num_seqs=len(seq_lens),
         num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
         num_blocks=num_blocks, partition_size=partition_size,

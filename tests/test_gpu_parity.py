@@ -79,6 +79,19 @@ def test_partition_sizes(partition_size):
     _run_and_check(workloads.gqa(3, num_seqs=10, max_len=2100, partition_size=partition_size))
 
 
+@pytest.mark.parametrize("block_size,partition_size", [
+    (16, 16), (16, 48), (16, 80), (16, 1024), (16, 2048), (32, 32), (32, 96), (32, 2048)])
+def test_fp8_group8_partitions(block_size, partition_size):
+    """FP8 KV with eight query heads per kv head: partitions of one block, of
+    an odd number of blocks (a 32-token step that crosses the partition end),
+    and of more than 64 blocks."""
+    lens = [1, 31, 33, 47, 100, 511, 700, 1025, 2100, 2600]
+    wl = build_decode_workload(f"fp8g8_{block_size}_{partition_size}", 9, seq_lens=lens, num_heads=64,
+                               num_kv_heads=8, head_dim=128, block_size=block_size, kv_dtype="fp8_e4m3",
+                               q_dtype="bf16", spare_blocks=4, num_copy_pairs=3, partition_size=partition_size)
+    _run_and_check(wl)
+
+
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025]
 
 
@@ -91,7 +104,9 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025]
     ("f32", "f32", 4, 4, 64, 16),
     ("f32", "f32", 8, 4, 128, 32),
     ("fp8_e4m3", "bf16", 64, 8, 128, 16),
+    ("fp8_e4m3", "bf16", 64, 8, 128, 32),
     ("fp8_e4m3", "bf16", 16, 4, 64, 32),
+    ("fp8_e4m3", "bf16", 16, 2, 128, 16),
 ])
 def test_edge_lengths_and_shapes(kv, q, heads, kv_heads, dim, block):
     wl = build_decode_workload(f"edge_{kv}_{heads}_{kv_heads}_{dim}_{block}", 5, seq_lens=EDGE_LENS,
@@ -199,5 +214,38 @@ def test_one_hot_probe_selects_value_bitwise(position):
     torch.cuda.synchronize()
     got = case.out[i, g * G:(g + 1) * G].cpu().numpy()
     vj = torch.from_numpy(wl.values[lo + j, g].view(np.int16)).view(torch.bfloat16).float().numpy()
+    for h in range(G):
+        assert np.array_equal(got[h], vj), f"head {h}: output is not exactly v[{j}]"
+
+
+@pytest.mark.parametrize("block_size", [16, 32])
+@pytest.mark.parametrize("position", [0, 31, 32, 511, 512, 1000, "last"])
+def test_one_hot_probe_fp8_group8(block_size, position):
+    """FP8 KV, eight query heads per kv head: a key whose score beats every
+    other by far more than 200 selects its dequantized value exactly."""
+    lens = [700, 1037, 33]
+    wl = build_decode_workload("probe8", 8, seq_lens=lens, num_heads=64, num_kv_heads=8, head_dim=128,
+                               block_size=block_size, kv_dtype="fp8_e4m3", q_dtype="bf16", spare_blocks=4,
+                               num_copy_pairs=2, partition_size=512)
+    i, g, G, T = 1, 5, 8, 1037
+    j = T - 1 if position == "last" else position
+    lo = int(wl.token_offsets[i])
+    wl.keys[lo:lo + T, g, 0] = 0
+    wl.step_keys_src[i, g, 0] = 0
+    if j == T - 1:
+        wl.step_keys_src[i, g, 0] = _bf16_bits(1.0e6)  # saturates to the largest code, 448
+    else:
+        wl.keys[lo + j, g, 0] = 0x7E  # 448
+    wl.q[i, g * G:(g + 1) * G, :] = 0
+    wl.q[i, g * G:(g + 1) * G, 0] = _bf16_bits(16384.0)
+    case = DeviceCase(wl)
+    case.run_step()
+    torch.cuda.synchronize()
+    got = case.out[i, g * G:(g + 1) * G].cpu().numpy()
+    kc, vc = oracle_pools(wl)
+    blk = int(wl.block_tables[i, j // block_size])
+    assert oracle.decode_elements(kc[blk, g, j % block_size, :1], "fp8_e4m3")[0] == 448.0
+    vj = (oracle.decode_elements(vc[blk, g, j % block_size], "fp8_e4m3") * np.float64(wl.v_scale[g])).astype(
+        np.float32)
     for h in range(G):
         assert np.array_equal(got[h], vj), f"head {h}: output is not exactly v[{j}]"

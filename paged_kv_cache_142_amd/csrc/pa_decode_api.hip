@@ -79,67 +79,140 @@ __global__ void __launch_bounds__(PLAN_THREADS) decode_plan_kernel(const DecodeA
     }
 }
 
-// Wave-wide max and sum (every lane receives the result).
+// Wave-wide max (every lane receives the result).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
     return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
+
+constexpr int REDUCE_THREADS = 256;
+constexpr int REDUCE_UNROLL = 8;
+
+// Merge the partition states of each (sequence, query head) row with the
+// log-sum-exp rule: M = max_p m_p, L = sum_p 2^(m_p - M) l_p, out = sum_p
+// 2^(m_p - M) acc_p / L (m_p is in log2 units).
+//
+// A row takes TPR = (D / 4) * RG threads: thread (pg, c4) owns columns
+// 4 c4 .. 4 c4 + 3 of partitions pg, pg + RG, pg + 2 RG, ..., loaded
+// REDUCE_UNROLL at a time so that many loads are in flight; the first batch
+// is loaded before the row maximum is known.  RG (partition groups per row)
+// is chosen from the largest partition count, so short rows share a
+// workgroup instead of idling most of one.  The groups' sums are added in
+// group order, so the result does not depend on timing.  Also writes the
+// rows the partition kernel does not: empty sequences (zeros) and invalid
+// ones (NaN).
+template <int D, int RG>
+__global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const DecodeArgs a) {
+    constexpr int C4 = D / 4;
+    constexpr int TPR = C4 * RG;
+    constexpr int RPW = REDUCE_THREADS / TPR;  // rows per workgroup
+    constexpr int U = REDUCE_UNROLL;
+    static_assert(REDUCE_THREADS % TPR == 0, "rows must tile the workgroup");
+    __shared__ float red_m[RPW][RG];
+    __shared__ float red_l[RPW][RG];
+    __shared__ float4 red_a[RPW][RG][C4];
+    const int tid = threadIdx.x;
+    const int rw = tid / TPR;
+    const int rt = tid - rw * TPR;
+    const int pg = rt / C4;
+    const int c4 = rt - pg * C4;
+    const size_t row = (size_t)blockIdx.x * RPW + rw;
+    const bool in_grid = row < (size_t)a.num_seqs * a.num_heads;
+    const int seq = in_grid ? (int)(row / a.num_heads) : 0;
+    const int T = in_grid ? a.seq_lens[seq] : 0;
+    auto store4 = [&](float4 o) {
+        const size_t idx = row * D + 4 * c4;
+        store_out(a.out, a.out_dtype, idx, o.x);
+        store_out(a.out, a.out_dtype, idx + 1, o.y);
+        store_out(a.out, a.out_dtype, idx + 2, o.z);
+        store_out(a.out, a.out_dtype, idx + 3, o.w);
+    };
+    const bool bad = T < 0 || T > a.max_seq_len || (T + a.block_size - 1) / a.block_size > a.max_blocks_per_seq;
+    if (in_grid && pg == 0 && (bad || T == 0)) {
+        const float v = bad ? __builtin_nanf("") : 0.f;
+        store4(float4{v, v, v, v});
+    }
+    // rows of one partition were finished by the partition kernel
+    const int n_parts = (!in_grid || bad || T == 0) ? 0 : (T + a.partition_size - 1) / a.partition_size;
+    const bool merge = n_parts > 1;
+    const size_t base = row * a.max_partitions;
+    const float* pm = a.part_m + base;
+    const float* pl = a.part_l + base;
+    const float4* pacc = (const float4*)(a.part_acc + base * D) + c4;
+
+    float mv[U], lv[U];
+    float4 av[U];
+    auto load_batch = [&](int p0) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * RG;
+            const bool have = merge && p < n_parts;
+            mv[u] = have ? pm[p] : -INFINITY;
+            lv[u] = have ? pl[p] : 0.f;
+            av[u] = have ? pacc[(size_t)p * C4] : float4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    float4 A = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    auto add_batch = [&](int p0, float M) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = merge && p0 + u * RG < n_parts ? fast_exp2(mv[u] - M) : 0.f;
+            L = fmaf(w, lv[u], L);
+            A.x = fmaf(w, av[u].x, A.x);
+            A.y = fmaf(w, av[u].y, A.y);
+            A.z = fmaf(w, av[u].z, A.z);
+            A.w = fmaf(w, av[u].w, A.w);
+        }
+    };
+
+    load_batch(pg);
+    float mx = mv[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mx = fmaxf(mx, mv[u]);
+    for (int p = pg + RG * U; merge && p < n_parts; p += RG) mx = fmaxf(mx, pm[p]);
+    if (c4 == 0) red_m[rw][pg] = mx;
+    __syncthreads();
+    float M = red_m[rw][0];
+#pragma unroll
+    for (int r = 1; r < RG; ++r) M = fmaxf(M, red_m[rw][r]);
+    add_batch(pg, M);
+    for (int p0 = pg + RG * U; merge && p0 < n_parts; p0 += RG * U) {
+        load_batch(p0);
+        add_batch(p0, M);
+    }
+    red_a[rw][pg][c4] = A;
+    if (c4 == 0) red_l[rw][pg] = L;
+    __syncthreads();
+    if (merge && pg == 0) {
+        float4 S = red_a[rw][0][c4];
+        float Ls = red_l[rw][0];
+#pragma unroll
+        for (int r = 1; r < RG; ++r) {
+            const float4 v = red_a[rw][r][c4];
+            S.x += v.x; S.y += v.y; S.z += v.z; S.w += v.w;
+            Ls += red_l[rw][r];
+        }
+        store4(float4{S.x / Ls, S.y / Ls, S.z / Ls, S.w / Ls});
+    }
 }
 
-// Merge the partition states of one (sequence, query head); one thread per
-// output element, D threads.  Partition states are fetched 64 at a time with
-// one vector load (lane p holds partition p), merged across the wave, and
-// the per-partition weights broadcast with readlane; groups of 64 are folded
-// with the same log-sum-exp rule in index order, so the result is
-// deterministic.  Also writes the rows the partition kernel does not: empty
-// sequences (zeros) and invalid ones (NaN).
+template <int D, int RG>
+static void launch_reduce(const DecodeArgs& a, hipStream_t stream) {
+    constexpr int RPW = REDUCE_THREADS / (D / 4 * RG);
+    const size_t rows = (size_t)a.num_seqs * a.num_heads;
+    const dim3 grid((unsigned)((rows + RPW - 1) / RPW));
+    hipLaunchKernelGGL((decode_reduce_kernel<D, RG>), grid, dim3(REDUCE_THREADS), 0, stream, a);
+}
+
 template <int D>
-__global__ void __launch_bounds__(D) decode_reduce_kernel(const DecodeArgs a) {
-    const int seq = blockIdx.x / a.num_heads;
-    const int hq = blockIdx.x - seq * a.num_heads;
-    const int d = threadIdx.x;
-    const int lane = d & 63;
-    const int T = a.seq_lens[seq];
-    const size_t row = (size_t)seq * a.num_heads + hq;
-    float o;
-    if (T < 0 || T > a.max_seq_len || (T + a.block_size - 1) / a.block_size > a.max_blocks_per_seq) {
-        o = __builtin_nanf("");
-    } else if (T == 0) {
-        o = 0.f;
-    } else {
-        const int n_parts = (T + a.partition_size - 1) / a.partition_size;
-        if (n_parts == 1) return;  // finished by the partition kernel
-        const size_t base = row * a.max_partitions;
-        float M = -INFINITY, L = 0.f, A = 0.f;
-        for (int p0 = 0; p0 < n_parts; p0 += 64) {
-            const int np = min(64, n_parts - p0);
-            const bool have = lane < np;
-            const float mp = have ? a.part_m[base + p0 + lane] : -INFINITY;
-            const float lp = have ? a.part_l[base + p0 + lane] : 0.f;
-            const float Mg = wave_max(mp);  // finite: every partition holds tokens
-            const float Mn = fmaxf(M, Mg);
-            const float wp = have ? fast_exp2(mp - Mn) : 0.f;
-            const float Lg = wave_sum(wp * lp);
-            const float f = fast_exp2(M - Mn);  // 0 on the first group (M = -inf)
-            float Ag = 0.f;
-            const float* accp = a.part_acc + (base + p0) * D + d;
-#pragma unroll 8
-            for (int p = 0; p < np; ++p) {
-                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), p));
-                Ag = fmaf(w, accp[(size_t)p * D], Ag);
-            }
-            L = L * f + Lg;
-            A = A * f + Ag;
-            M = Mn;
-        }
-        o = A / L;
-    }
-    store_out(a.out, a.out_dtype, row * D + d, o);
+static void launch_reduce_for(const DecodeArgs& a, hipStream_t stream) {
+    const int mp = a.max_partitions;
+    if (mp <= REDUCE_UNROLL) launch_reduce<D, 1>(a, stream);
+    else if (mp <= 2 * REDUCE_UNROLL) launch_reduce<D, 2>(a, stream);
+    else if (mp <= 4 * REDUCE_UNROLL) launch_reduce<D, 4>(a, stream);
+    else launch_reduce<D, 8>(a, stream);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -239,11 +312,10 @@ static int run_partition(const Prepared& pr, hipStream_t stream) {
 }
 
 static int run_reduce(const Prepared& pr, hipStream_t stream) {
-    const dim3 grid((unsigned)(pr.args.num_seqs * pr.args.num_heads));
     if (pr.head_dim == 128)
-        hipLaunchKernelGGL(decode_reduce_kernel<128>, grid, dim3(128), 0, stream, pr.args);
+        launch_reduce_for<128>(pr.args, stream);
     else
-        hipLaunchKernelGGL(decode_reduce_kernel<64>, grid, dim3(64), 0, stream, pr.args);
+        launch_reduce_for<64>(pr.args, stream);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -172,10 +172,10 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
 #pragma unroll
-        for (int j = 0; j < Sh::DMA_PER_TILE; ++j) dma16_to_lds(kc + tile + koff[j], dst + j * 1024);
+        for (int j = 0; j < Sh::DMA_PER_TILE; ++j) dma16_to_lds_stream(kc + tile + koff[j], dst + j * 1024);
 #pragma unroll
         for (int j = 0; j < Sh::DMA_PER_TILE; ++j)
-            dma16_to_lds(vc + tile + (size_t)j * 1024 + lane * 16, dst + TILE + j * 1024);
+            dma16_to_lds_stream(vc + tile + (size_t)j * 1024 + lane * 16, dst + TILE + j * 1024);
     };
 
     float m = -INFINITY, l = 0.f;  // per head hl (uniform over its 16 lanes)
@@ -327,10 +327,10 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
         } else {
             const size_t pidx = row * a.max_partitions + part;
             if (d == 0) {
-                a.part_m[pidx] = bad ? __builtin_nanf("") : M;
-                a.part_l[pidx] = bad ? __builtin_nanf("") : L;
+                store_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
+                store_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
             }
-            a.part_acc[pidx * D + d] = bad ? __builtin_nanf("") : A * vs;
+            store_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     }
 }

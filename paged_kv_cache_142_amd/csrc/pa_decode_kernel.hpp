@@ -359,9 +359,9 @@ decode_partition_kernel(const DecodeArgs a) {
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)lane * 16;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
 #pragma unroll
-        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds(kc + tile + i * 1024, dst + i * 1024);
+        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds_stream(kc + tile + i * 1024, dst + i * 1024);
 #pragma unroll
-        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds(vc + tile + i * 1024, dst + TILE + i * 1024);
+        for (int i = 0; i < Sh::DMA_PER_TILE; ++i) dma16_to_lds_stream(vc + tile + i * 1024, dst + TILE + i * 1024);
     };
 
     float m[G], l[G], acc[G][8];
@@ -478,10 +478,10 @@ decode_partition_kernel(const DecodeArgs a) {
         } else {
             const size_t pidx = row * a.max_partitions + part;
             if (d == 0) {
-                a.part_m[pidx] = bad ? __builtin_nanf("") : M;
-                a.part_l[pidx] = bad ? __builtin_nanf("") : L;
+                store_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
+                store_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
             }
-            a.part_acc[pidx * D + d] = bad ? __builtin_nanf("") : A * vs;
+            store_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     };
 

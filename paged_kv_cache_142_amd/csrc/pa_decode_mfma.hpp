@@ -210,10 +210,10 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < Sh::DMA_PER_TILE; ++j)
-                dma16_to_lds(kc + tile + koff[j], dst + b * TILE + j * 1024);
+                dma16_to_lds_stream(kc + tile + koff[j], dst + b * TILE + j * 1024);
 #pragma unroll
             for (int j = 0; j < Sh::DMA_PER_TILE; ++j)
-                dma16_to_lds(vc + tile + voff[j], dst + Sh::UNIT_BYTES + b * TILE + j * 1024);
+                dma16_to_lds_stream(vc + tile + voff[j], dst + Sh::UNIT_BYTES + b * TILE + j * 1024);
         }
     };
 
@@ -387,10 +387,10 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
         } else {
             const size_t pidx = row * a.max_partitions + part;
             if (d == 0) {
-                a.part_m[pidx] = bad ? __builtin_nanf("") : M;
-                a.part_l[pidx] = bad ? __builtin_nanf("") : L;
+                store_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
+                store_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
             }
-            a.part_acc[pidx * D + d] = bad ? __builtin_nanf("") : A * vs;
+            store_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     }
 }

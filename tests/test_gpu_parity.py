@@ -92,6 +92,16 @@ def test_fp8_group8_partitions(block_size, partition_size):
     _run_and_check(wl)
 
 
+def test_fp8_group8_many_units_per_workgroup():
+    """Partitions of one block over long sequences: more (sequence, kv head,
+    partition) units than 64 per resident workgroup."""
+    lens = [9000] * 7 + [8191]
+    wl = build_decode_workload("fp8g8_many", 12, seq_lens=lens, num_heads=64, num_kv_heads=8, head_dim=128,
+                               block_size=16, kv_dtype="fp8_e4m3", q_dtype="bf16", spare_blocks=4,
+                               num_copy_pairs=2, partition_size=16)
+    _run_and_check(wl, rows=[0, 3, 7])
+
+
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025]
 
 
@@ -249,3 +259,31 @@ def test_one_hot_probe_fp8_group8(block_size, position):
         np.float32)
     for h in range(G):
         assert np.array_equal(got[h], vj), f"head {h}: output is not exactly v[{j}]"
+
+
+@pytest.mark.parametrize("kv,q,heads,kv_heads,block", [
+    ("fp8_e4m3", "bf16", 64, 8, 16),
+    ("fp8_e4m3", "bf16", 64, 8, 32),
+    ("bf16", "bf16", 32, 8, 16),
+    ("f16", "f16", 8, 8, 16),
+])
+def test_out_of_range_block_id_gives_nan_row(kv, q, heads, kv_heads, block):
+    """A block id outside the pool (too large, or negative) is never used as an
+    address: its sequence gets rows of NaN and the other rows are unaffected."""
+    lens = [1500, 2100, 700, 1200, 333]
+    wl = build_decode_workload(f"badid_{kv}_{heads}_{block}", 11, seq_lens=lens, num_heads=heads,
+                               num_kv_heads=kv_heads, head_dim=128, block_size=block, kv_dtype=kv, q_dtype=q,
+                               spare_blocks=4, num_copy_pairs=2, partition_size=512)
+    case = DeviceCase(wl)
+    case.run_cache_ops()
+    bt = case.block_tables.clone()
+    bt[1, 40] = wl.num_blocks + 7  # inside a middle partition of sequence 1
+    bt[2, 5] = -3                  # inside the first partition of sequence 2
+    case.decode(block_tables=bt)
+    torch.cuda.synchronize()
+    got = out_as_f64(case.out)
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all(), "rows with a bad block id must be NaN"
+    kc, vc = oracle_pools(wl)
+    rows = [0, 3, 4]
+    want = oracle_out(wl, kc, vc, rows=rows)
+    assert_close(got[rows], want, TOL[kv], f"rows next to bad ids ({kv}, B={block})")

@@ -74,9 +74,22 @@ def test_fp8_small(block_size, seed):
     _run_and_check(workloads.long_fp8(seed, block_size=block_size, num_seqs=3, seq_len=1300))
 
 
-@pytest.mark.parametrize("partition_size", [16, 64, 256, 1024])
+@pytest.mark.parametrize("partition_size", [16, 64, 256, 1024, 4096, 8192])
 def test_partition_sizes(partition_size):
-    _run_and_check(workloads.gqa(3, num_seqs=10, max_len=2100, partition_size=partition_size))
+    """Four query heads per kv head, partitions from one block to more than
+    64 blocks per wave."""
+    _run_and_check(workloads.gqa(3, num_seqs=10, max_len=9000 if partition_size > 1024 else 2100,
+                                 partition_size=partition_size))
+
+
+def test_gqa4_one_block_partitions_long_sequences():
+    """Partitions of one block over long sequences: hundreds of partition
+    states per row for the reduce."""
+    lens = [9000] * 7 + [8191]
+    wl = build_decode_workload("gqa4_many", 13, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, kv_dtype="bf16", q_dtype="bf16", spare_blocks=4,
+                               num_copy_pairs=2, partition_size=16)
+    _run_and_check(wl, rows=[0, 3, 7])
 
 
 @pytest.mark.parametrize("block_size,partition_size", [
@@ -92,9 +105,9 @@ def test_fp8_group8_partitions(block_size, partition_size):
     _run_and_check(wl)
 
 
-def test_fp8_group8_many_units_per_workgroup():
-    """Partitions of one block over long sequences: more (sequence, kv head,
-    partition) units than 64 per resident workgroup."""
+def test_fp8_group8_one_block_partitions_long_sequences():
+    """Partitions of one block over long sequences: hundreds of partition
+    states per row for the reduce."""
     lens = [9000] * 7 + [8191]
     wl = build_decode_workload("fp8g8_many", 12, seq_lens=lens, num_heads=64, num_kv_heads=8, head_dim=128,
                                block_size=16, kv_dtype="fp8_e4m3", q_dtype="bf16", spare_blocks=4,
@@ -109,6 +122,9 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025]
     ("bf16", "bf16", 32, 8, 128, 16),
     ("bf16", "bf16", 8, 4, 64, 32),
     ("bf16", "bf16", 16, 2, 128, 32),
+    ("bf16", "bf16", 16, 4, 64, 16),
+    ("f16", "f16", 32, 8, 64, 32),
+    ("f16", "f16", 32, 8, 128, 32),
     ("f16", "f16", 4, 4, 128, 16),
     ("f16", "f16", 8, 1, 64, 16),
     ("f32", "f32", 4, 4, 64, 16),
@@ -169,6 +185,31 @@ def test_mha_full_size_sampled():
 def test_long_fp8_full_size_sampled(block_size):
     wl = workloads.long_fp8(0, block_size=block_size)
     _run_and_check(wl, rows=[0, 7, 15])
+
+
+def test_empty_and_invalid_rows():
+    """Empty sequences get zero rows and a sequence whose length exceeds
+    max_seq_len gets a NaN row; every other row matches the oracle."""
+    lens = [0, 700, 0, 1500, 2000, 0, 33]
+    wl = build_decode_workload("fill_rows", 10, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                               block_size=16, kv_dtype="bf16", q_dtype="bf16", spare_blocks=4,
+                               num_copy_pairs=2, partition_size=256)
+    case = DeviceCase(wl)
+    case.run_cache_ops()
+    case.out.fill_(123.0)
+    bad_lens = case.seq_lens.clone()
+    bad_lens[3] = wl.max_seq_len + 1  # beyond the host bound: invalid
+    args = case.decode_args()
+    args["seq_lens"] = bad_lens
+    pa.pa_decode(**args)
+    torch.cuda.synchronize()
+    got = out_as_f64(case.out)
+    for i in (0, 2, 5):
+        assert np.array_equal(got[i], np.zeros_like(got[i])), f"row {i} of an empty sequence"
+    assert np.isnan(got[3]).all(), "row of an invalid sequence must be NaN"
+    kc, vc = oracle_pools(wl)
+    rows = [1, 4, 6]
+    assert_close(got[rows], oracle_out(wl, kc, vc, rows=rows), TOL["bf16"], "rows beside empty/invalid ones")
 
 
 # ------------------------------------------------ indexing, determinism

@@ -291,6 +291,11 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.part_l = (float*)((char*)workspace + align256(rows * 4));
     a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
     a.plan = (int*)((char*)workspace + plan_offset(num_seqs, num_heads, head_dim, max_parts));
+#ifndef PA_NO_INLINE_PLAN
+    a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
+#else
+    a.inline_plan = 0;
+#endif
     pr.head_dim = head_dim;
     pr.group = group;
     pr.kv_dtype = kv_dtype;
@@ -300,8 +305,10 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
 
 static int run_partition(const Prepared& pr, hipStream_t stream) {
     if (pr.args.max_partitions == 0) return PA_OK;  // every sequence is empty
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pr.args);
-    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+    if (!pr.args.inline_plan) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pr.args);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+    }
     switch (pr.kv_dtype) {
         case PA_DTYPE_F32: return launch_partition_f32(pr.args, pr.head_dim, pr.group, stream);
         case PA_DTYPE_F16: return launch_partition_f16(pr.args, pr.head_dim, pr.group, stream);

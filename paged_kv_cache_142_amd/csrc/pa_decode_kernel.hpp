@@ -67,9 +67,75 @@ struct DecodeArgs {
     // partition) items, plan[PLAN_ITEMS_OFFSET + k] = seq * max_partitions +
     // partition of the k-th item, largest first.
     int* plan;
+    // 1: no plan kernel ran; every partition workgroup derives its item from
+    // seq_lens itself (at most 64 sequences and 64 blocks per partition).
+    int inline_plan;
 };
 
 constexpr int PLAN_ITEMS_OFFSET = 64;
+constexpr int INLINE_PLAN_MAX_SEQS = 64;
+constexpr int INLINE_PLAN_MAX_BLOCKS = 64;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (DPP row shifts
+// within rows of 16 lanes, then row broadcasts across rows).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// The k-th (sequence, partition) item of the largest-first order, computed
+// by one wavefront from the sequence lengths (one sequence per lane):
+// first every partition of full size PB = partition_size / block_size, in
+// (sequence, partition) order; then the partial last partitions, by size in
+// blocks from PB - 1 down to 1, sequences in index order within a size.
+// Sequences that are empty or invalid have no items.  Returns false when k
+// is past the last item.  The partial partitions are ranked by a radix
+// select on the key (PB - size) * 64 + sequence, one ballot per key bit.
+__device__ __forceinline__ bool inline_plan_item(const DecodeArgs& a, int k, int& seq, int& part) {
+    const int lane = threadIdx.x & 63;
+    const int B = a.block_size;
+    const int P = a.partition_size;
+    const int PB = P / B;
+    const int T = lane < a.num_seqs ? a.seq_lens[lane] : 0;
+    const bool ok = T > 0 && T <= a.max_seq_len && (T + B - 1) / B <= a.max_blocks_per_seq;
+    const int np = ok ? (T + P - 1) / P : 0;
+    const int rem = ok ? (T + B - 1) / B - (np - 1) * PB : 0;  // blocks of the last partition
+    const int nfull = ok ? np - (rem < PB ? 1 : 0) : 0;
+    const int incl = wave_inclusive_sum(nfull);
+    const int F = __builtin_amdgcn_readlane(incl, 63);
+    uint64_t cand = __builtin_amdgcn_ballot_w64(ok && rem < PB);  // sequences with a partial partition
+    if (k >= F + __builtin_popcountll(cand)) return false;
+    if (k < F) {
+        const uint64_t past = __builtin_amdgcn_ballot_w64(incl > k);
+        if (past == 0) return false;  // cannot happen for k < F; keeps every index in range regardless
+        const int s = __builtin_ctzll(past);
+        seq = s;
+        part = k - (__builtin_amdgcn_readlane(incl, s) - __builtin_amdgcn_readlane(nfull, s));
+        return s < a.num_seqs && part >= 0 && part < __builtin_amdgcn_readlane(np, s);
+    }
+    k -= F;
+    const int key = ((PB - rem) << 6) | lane;  // PB <= 64: 12 bits
+#pragma unroll
+    for (int b = 11; b >= 0; --b) {
+        const uint64_t zero = cand & __builtin_amdgcn_ballot_w64(((key >> b) & 1) == 0);
+        const int c = __builtin_popcountll(zero);
+        if (k < c) {
+            cand = zero;
+        } else {
+            k -= c;
+            cand &= ~zero;
+        }
+    }
+    if (cand == 0) return false;  // cannot happen for k < popcount; as above
+    seq = __builtin_ctzll(cand);
+    part = __builtin_amdgcn_readlane(np, seq) - 1;
+    return seq < a.num_seqs && part >= 0;
+}
 
 // The (sequence, kv head, partition) of this partition workgroup: workgroup
 // x = item * num_kv_heads + kv head, items in the plan's order.  Returns
@@ -77,6 +143,7 @@ constexpr int PLAN_ITEMS_OFFSET = 64;
 __device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, int& seq, int& kvh, int& part) {
     const int item = blockIdx.x / a.num_kv_heads;
     kvh = blockIdx.x - item * a.num_kv_heads;
+    if (a.inline_plan) return inline_plan_item(a, item, seq, part);
     if (item >= a.plan[0]) return false;
     const int code = a.plan[PLAN_ITEMS_OFFSET + item];
     seq = code / a.max_partitions;

@@ -82,6 +82,19 @@ def test_partition_sizes(partition_size):
                                  partition_size=partition_size))
 
 
+@pytest.mark.parametrize("kv,q,heads,num_seqs", [("bf16", "bf16", 32, 65), ("bf16", "bf16", 32, 64),
+                                                  ("fp8_e4m3", "bf16", 64, 80), ("f16", "f16", 8, 100)])
+def test_work_order_sources(kv, q, heads, num_seqs):
+    """Up to 64 sequences, partition workgroups derive the largest-first work
+    order from the lengths themselves; beyond that a plan kernel writes it.
+    Both orders cover every (sequence, partition) once."""
+    lens = np.random.default_rng(num_seqs).integers(0, 1400, size=num_seqs)
+    wl = build_decode_workload(f"order_{kv}_{num_seqs}", 14, seq_lens=lens, num_heads=heads, num_kv_heads=8,
+                               head_dim=128, block_size=16, kv_dtype=kv, q_dtype=q, spare_blocks=4,
+                               num_copy_pairs=2, partition_size=256)
+    _run_and_check(wl)
+
+
 def test_gqa4_one_block_partitions_long_sequences():
     """Partitions of one block over long sequences: hundreds of partition
     states per row for the reduce."""

@@ -6,6 +6,9 @@ block copies (``pa_copy_blocks``), and the decode itself
 (``pa_decode_partition`` then ``pa_decode_reduce``, i.e. ``pa_decode``).
 Inputs are resident in HBM before the timed region.  Throughput is the
 effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
+Also reported: ``pa_decode`` alone, called back to back (``decode_alone_*``),
+and per-call durations from a second loop with HIP events around each call
+(``kernels_us``), from which the roofline of the partition launch is taken.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
@@ -276,6 +279,19 @@ def main():
     gpu_ms = start.elapsed_time(stop)
     ms_per_step = gpu_ms / args.steps
 
+    # pa_decode alone, back to back (no other launches, no markers between calls)
+    decode_call = dev.pa.prepared("pa_decode", **dev.dargs)
+    for _ in range(args.warmup):
+        decode_call()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record()
+    for _ in range(args.steps):
+        decode_call()
+    d1.record()
+    torch.cuda.synchronize()
+    decode_alone_us = d0.elapsed_time(d1) / args.steps * 1e3
+
     # per-kernel durations: the same steps, eager, with an event around each launch
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -309,12 +325,15 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "seqs_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "decode_only_GBs": round(kv_bytes / (k_us["decode"] * 1e-6) / 1e9, 2),
+        "decode_alone_us": round(decode_alone_us, 2),
+        "decode_alone_GBs": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9, 2),
+        "decode_alone_hbm_frac": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
         "decode_partition_us_p10_p90": [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
-        "roofline": {"kernel": "pa_decode_partition launch (decode_plan_kernel + decode partition kernel)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "pa_decode_partition launch (the partition kernel; preceded by decode_plan_kernel "
+                               "above 64 sequences)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }

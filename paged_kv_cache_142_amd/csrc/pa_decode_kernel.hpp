@@ -621,7 +621,7 @@ int launch_partition_fp8_bf16q(const DecodeArgs& a, int head_dim, int group, hip
 
 // Waves per workgroup and ring depth of the default variant.
 #ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
+#define PA_DECODE_WAVES 2
 #endif
 #ifndef PA_DECODE_STAGES
 #define PA_DECODE_STAGES 2

@@ -408,7 +408,7 @@ int launch_partition_mfma8(const DecodeArgs& a, hipStream_t stream) {
 }
 
 #ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 4
+#define PA_MFMA_WAVES 2
 #endif
 #ifndef PA_MFMA_STAGES
 #define PA_MFMA_STAGES 2

@@ -6,6 +6,9 @@ block copies (``pa_copy_blocks``), and the decode itself
 (``pa_decode_partition`` then ``pa_decode_reduce``, i.e. ``pa_decode``).
 Inputs are resident in HBM before the timed region.  Throughput is the
 effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
+By default two copies of the K/V pool alternate between steps, so that no
+step finds the previous step's K/V in the 256 MB Infinity Cache (on MI355X
+this costs about 1% against re-reading one pool; ``--pools 1`` for that).
 Also reported: ``pa_decode`` alone, called back to back (``decode_alone_*``),
 and per-call durations from a second loop with HIP events around each call
 (``kernels_us``), from which the roofline of the partition launch is taken.
@@ -47,6 +50,9 @@ def _parse():
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
+    p.add_argument("--pools", type=int, default=2,
+                   help="copies of the K/V pool; step i uses copy i %% pools, so back-to-back steps read K/V that "
+                        "the 256 MB Infinity Cache does not hold (1: every step re-reads the same pool)")
     p.add_argument("--graph", action="store_true",
                    help="replay the step as a captured HIP graph (the four launches) instead of eager calls")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -89,7 +95,14 @@ def _describe(wl):
 
 
 class Device:
-    def __init__(self, wl):
+    """The workload resident on the GPU and the step's prepared calls.
+
+    pools > 1 keeps that many copies of the K/V pool; step i runs on copy
+    i % pools, so that back-to-back steps do not find the previous step's
+    K/V in the 256 MB Infinity Cache (MALL) once the copies together exceed it.
+    """
+
+    def __init__(self, wl, pools=1):
         import torch
         import paged_kv_cache_142_amd as pa
         self.pa, self.torch, self.wl = pa, torch, wl
@@ -137,23 +150,30 @@ class Device:
                           scale=float(wl.scale), partition_size=wl.partition_size, workspace=self.ws,
                           k_scale=self.k_scale, v_scale=self.v_scale, kv_dtype=kv)
         self.dargs = dargs
-        # identical calls every step: marshal the C arguments once
-        self.calls = self._make_calls()
+        self.pools = [(self.k_cache, self.v_cache)] + [(self.k_cache.clone(), self.v_cache.clone())
+                                                        for _ in range(pools - 1)]
+        # identical calls every step: marshal the C arguments once per pool copy
+        self.call_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
+        self.decode_calls = [pa.prepared("pa_decode", **dict(self.dargs, k_cache=kc, v_cache=vc))
+                             for kc, vc in self.pools]
+        self.calls = self.call_sets[0]
         torch.cuda.synchronize()
 
-    def _make_calls(self):
+    def _make_calls(self, k_cache=None, v_cache=None):
         pa, kv = self.pa, self.kv
-        scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, self.k_cache,
-                               self.v_cache, self.k_scale, self.v_scale, self.step_slots)
+        kc = self.k_cache if k_cache is None else k_cache
+        vc = self.v_cache if v_cache is None else v_cache
+        dargs = dict(self.dargs, k_cache=kc, v_cache=vc)
+        scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, kc, vc,
+                               self.k_scale, self.v_scale, self.step_slots)
                    if self.quantize_step else
-                   pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, self.k_cache, self.v_cache,
+                   pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, kc, vc,
                                self.step_slots, kv_dtype=kv))
         return [
             scatter,
-            pa.prepared("pa_copy_blocks", self.k_cache, self.v_cache, self.pairs, kv_dtype=kv)
-            if self.pairs.numel() else (lambda: None),
-            pa.prepared("pa_decode_partition", **self.dargs),
-            pa.prepared("pa_decode_reduce", **self.dargs),
+            pa.prepared("pa_copy_blocks", kc, vc, self.pairs, kv_dtype=kv) if self.pairs.numel() else (lambda: None),
+            pa.prepared("pa_decode_partition", **dargs),
+            pa.prepared("pa_decode_reduce", **dargs),
         ]
 
     def capture(self):
@@ -172,13 +192,14 @@ class Device:
         torch.cuda.synchronize()
         return g
 
-    def step(self, ev=None):
+    def step(self, i=0, ev=None):
+        calls = self.call_sets[i % len(self.call_sets)]
         if ev is None:
-            for call in self.calls:
+            for call in calls:
                 call()
             return
         ev[0].record()
-        for k, call in enumerate(self.calls):
+        for k, call in enumerate(calls):
             call()
             ev[k + 1].record()
 
@@ -257,23 +278,26 @@ def main():
         copy_calibration(args.copy_calibration_mib, args.steps)
         return
     wl = _workload(args.config, args.seed, args.partition_size)
-    dev = Device(wl)
+    if args.graph and args.pools != 1:
+        print("--graph replays one captured step and cannot rotate pool copies; use --pools 1", file=sys.stderr)
+        sys.exit(2)
+    dev = Device(wl, pools=args.pools)
     graph = None
     if args.graph:  # one eager step first (one-time kernel attribute setup), then capture
         dev.step()
         torch.cuda.synchronize()
         graph = dev.capture()
-    run = graph.replay if graph is not None else dev.step
-    for _ in range(args.warmup):
-        run()
+    run = (lambda i: graph.replay()) if graph is not None else dev.step
+    for i in range(args.warmup):
+        run(i)
     torch.cuda.synchronize()
     # timed region: exactly K steps, no markers between the launches
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        run()
+    for i in range(args.steps):
+        run(i)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -281,14 +305,14 @@ def main():
     ms_per_step = gpu_ms / args.steps
 
     # pa_decode alone, back to back (no other launches, no markers between calls)
-    decode_call = dev.pa.prepared("pa_decode", **dev.dargs)
-    for _ in range(args.warmup):
-        decode_call()
+    npools = len(dev.decode_calls)
+    for i in range(args.warmup):
+        dev.decode_calls[i % npools]()
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     d0.record()
-    for _ in range(args.steps):
-        decode_call()
+    for i in range(args.steps):
+        dev.decode_calls[i % npools]()
     d1.record()
     torch.cuda.synchronize()
     decode_alone_us = d0.elapsed_time(d1) / args.steps * 1e3
@@ -297,7 +321,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        dev.step(evs[k])
+        dev.step(k, evs[k])
     torch.cuda.synchronize()
 
     def avg(a, b):
@@ -333,6 +357,7 @@ def main():
         "decode_partition_us_p10_p90": [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
+        "pool_copies": args.pools,
         "roofline": {"kernel": "pa_decode_partition launch (the partition kernel; preceded by decode_plan_kernel "
                                "above 64 sequences)", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

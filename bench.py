@@ -45,7 +45,8 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="gqa", choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny"])
+    p.add_argument("--config", default="gqa",
+                   choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -73,8 +74,72 @@ def copy_calibration(mib, steps):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
 
 
+def shared_prefix_step(seed, partition_size, prompt_len):
+    """The shared-prefix beam workload as one decode step.
+
+    8 prompts of ``prompt_len`` tokens, each forked into 6 beams by the host
+    block manager (every prompt block shared, reference count 6), then each
+    beam's suffix appended through it: the first write into a shared,
+    partially filled boundary block takes a private copy (copy-on-write).
+    The cached state before the step is what those copies and writes leave:
+    each private boundary block holds the prompt's tail rows and the beam's
+    own suffix.  The timed step scatters every beam's newest token, copies
+    as many blocks as copy-on-write needed (into spare blocks no table
+    references, so that repeating the step leaves the state unchanged) and
+    decodes.  Odd beams carry queries whose logits reach +-80.
+    """
+    import paged_kv_cache_142_amd as pa
+    import workloads
+    from workloads.generators import DecodeWorkload
+    sp = workloads.shared_prefix(seed, prompt_len=prompt_len)
+    B = sp.block_size
+    prompt_blocks = -(-prompt_len // B)
+    live = sp.num_prompts * prompt_blocks + sp.num_seqs * (-(-256 // B) + 2) + 8
+    bm = pa.BlockManager(live, B, free_order=np.random.default_rng(seed).permutation(live))
+    beams, cow = [], []
+    for k in range(sp.num_prompts):
+        root = bm.add_sequence()
+        for _ in range(prompt_len):
+            bm.append_slot(root)
+        beams += bm.fork(root, sp.beams)
+        bm.free_sequence(root)
+    for n, s in enumerate(beams):
+        for _ in range(int(sp.suffix_lens[n])):
+            _, pair = bm.append_slot(s)
+            if pair is not None:
+                cow.append(pair)
+    bm.check_invariants()
+    lens = np.array([bm.seq_len(s) for s in beams], np.int32)
+    tables = bm.tables_array(beams)
+    keys = np.concatenate([np.concatenate([sp.prompt_keys[n // sp.beams], sp.suffix_keys[n]]) for n in range(sp.num_seqs)])
+    values = np.concatenate([np.concatenate([sp.prompt_values[n // sp.beams], sp.suffix_values[n]])
+                             for n in range(sp.num_seqs)])
+    offsets = np.zeros(sp.num_seqs + 1, np.int64)
+    offsets[1:] = np.cumsum(lens.astype(np.int64))
+    slots = np.concatenate([tables[i, np.arange(t) // B].astype(np.int64) * B + np.arange(t) % B
+                            for i, t in enumerate(lens)])
+    spare = np.arange(live, live + len(cow), dtype=np.int64)
+    pairs = np.stack([np.array([c[0] for c in cow], np.int64), spare], axis=1) if cow else np.zeros((0, 2), np.int64)
+    return DecodeWorkload(
+        name=f"shared_prefix_{prompt_len}", seed=seed, kv_dtype=sp.kv_dtype, q_dtype=sp.q_dtype,
+        num_seqs=sp.num_seqs, num_heads=sp.num_heads, num_kv_heads=sp.num_kv_heads, head_dim=sp.head_dim,
+        block_size=B, num_blocks=live + len(cow), partition_size=partition_size, scale=sp.scale, seq_lens=lens,
+        block_tables=tables, token_offsets=offsets, keys=keys, values=values, slots=slots, q=sp.q, k_scale=None,
+        v_scale=None, copy_pairs=pairs)
+
+
+def unique_kv_bytes(wl):
+    """K+V bytes of the distinct cached tokens (a slot shared by several
+    sequences counts once)."""
+    return len(np.unique(wl.slots)) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+
+
 def _workload(name, seed, partition_size):
     import workloads
+    if name == "shared_prefix":
+        return shared_prefix_step(seed, partition_size, 1024)
+    if name == "shared_prefix_cow":
+        return shared_prefix_step(seed, partition_size, 1032)
     if name == "gqa":
         return workloads.gqa(seed, partition_size=partition_size)
     if name == "mha":
@@ -92,6 +157,12 @@ def _describe(wl):
             f"{wl.q_dtype} q, f32 out and accumulation, P={wl.partition_size}; step = scatter of "
             f"{wl.num_seqs} new tokens{' (bf16, quantized on write)' if wl.step_keys_src is not None else ''}"
             f" + copy of {len(wl.copy_pairs)} blocks + split-KV decode")
+
+
+def _first_per_slot(slots, rows):
+    """The rows, keeping the first of those that name the same slot."""
+    _, first = np.unique(slots[rows], return_index=True)
+    return rows[np.sort(first)]
 
 
 class Device:
@@ -120,8 +191,10 @@ class Device:
         self.v_cache = torch.zeros(wl.pool_shape(), dtype=view[wl.kv_dtype], device=dev)
         keys, values = up(wl.keys, wl.kv_dtype), up(wl.values, wl.kv_dtype)
         slots = torch.from_numpy(wl.slots).to(dev)
-        pre = torch.from_numpy(wl.prefill_rows()).to(dev)
-        step = torch.from_numpy(wl.step_rows()).to(dev)
+        # one row per slot: sequences that share a block (shared prefixes)
+        # list its rows once each, with identical contents
+        pre = torch.from_numpy(_first_per_slot(wl.slots, wl.prefill_rows())).to(dev)
+        step = torch.from_numpy(_first_per_slot(wl.slots, wl.step_rows())).to(dev)
         kv = "fp8_e4m3" if self.fp8 else None
         pa.pa_reshape_and_cache(keys[pre].contiguous(), values[pre].contiguous(), self.k_cache, self.v_cache,
                                 slots[pre].contiguous(), kv_dtype=kv)
@@ -363,6 +436,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }
+    if wl.name.startswith("shared_prefix"):
+        line["config"]["unique_kv_bytes_per_step"] = unique_kv_bytes(wl)
+        line["config"]["cache_assisted"] = ("prompt blocks are shared by 6 beams: the logical KV bytes are read "
+                                            "from far fewer distinct bytes, which fit in the Infinity Cache")
+        line["unique_kv_GBs"] = round(unique_kv_bytes(wl) / (ms_per_step * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -56,6 +56,9 @@ def _parse():
                         "the 256 MB Infinity Cache does not hold (1: every step re-reads the same pool)")
     p.add_argument("--graph", action="store_true",
                    help="replay the step as a captured HIP graph (the four launches) instead of eager calls")
+    p.add_argument("--swap-mib", type=int, default=0,
+                   help="instead of the benchmark, time pa_swap_blocks moving this many MiB of blocks to pinned "
+                        "host memory and back (host-link GB/s)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="instead of the benchmark, run a plain device copy of this many MiB per step "
                         "(reference for scaling the FETCH_SIZE/WRITE_SIZE counters)")
@@ -132,6 +135,40 @@ def unique_kv_bytes(wl):
     """K+V bytes of the distinct cached tokens (a slot shared by several
     sequences counts once)."""
     return len(np.unique(wl.slots)) * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+
+
+def swap_bandwidth(mib, steps):
+    """Host-link rate of pa_swap_blocks: the gqa block shape (8 kv heads x
+    16 rows x 128 bf16, 64 KiB of K+V per block), `mib` MiB of blocks moved
+    device -> pinned host and back, in a seeded random block order."""
+    import torch
+    import paged_kv_cache_142_amd as pa
+    per_block = 2 * 8 * 16 * 128 * 2
+    n = max(1, mib * (1 << 20) // per_block)
+    shape = (n, 8, 16, 128)
+    kc = torch.randn(shape, device="cuda").to(torch.bfloat16)
+    vc = torch.randn(shape, device="cuda").to(torch.bfloat16)
+    hk = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(0)
+    out_pairs = torch.from_numpy(np.stack([rng.permutation(n), rng.permutation(n)], 1).astype(np.int64)).cuda()
+    in_pairs = out_pairs.flip(1).contiguous()
+    times = {}
+    for name, args in (("out", (kc, vc, hk, hv, out_pairs)), ("in", (hk, hv, kc, vc, in_pairs))):
+        pa.pa_swap_blocks(*args)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            pa.pa_swap_blocks(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / steps * 1e-3
+    byts = n * per_block
+    print(json.dumps({"swap_blocks": n, "bytes_per_direction": byts,
+                      "swap_out_GBs": round(byts / times["out"] / 1e9, 2),
+                      "swap_in_GBs": round(byts / times["in"] / 1e9, 2),
+                      "swap_out_ms": round(times["out"] * 1e3, 3), "swap_in_ms": round(times["in"] * 1e3, 3)}))
 
 
 def _workload(name, seed, partition_size):
@@ -349,6 +386,9 @@ def main():
     import torch
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib, args.steps)
+        return
+    if args.swap_mib:
+        swap_bandwidth(args.swap_mib, args.steps)
         return
     wl = _workload(args.config, args.seed, args.partition_size)
     if args.graph and args.pools != 1:

@@ -63,7 +63,8 @@ typedef enum pa_status {
     PA_ERR_DTYPE = -3,       /* unknown dtype code or unsupported dtype combination */
     PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, block_size, GQA group */
     PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_size()   */
-    PA_ERR_LAUNCH = -6       /* the HIP runtime rejected a kernel launch           */
+    PA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch           */
+    PA_ERR_MEMORY = -7       /* a pool the GPU cannot address (pa_swap_blocks)      */
 } pa_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -142,6 +143,39 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, int src_dtype, 
 int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int num_pairs,
                    int num_kv_heads, int head_dim, int block_size, int num_blocks, int kv_dtype,
                    void* stream);
+
+/*
+ * pa_swap_blocks -- move whole blocks between two pools: the device pool
+ * and a pool in pinned host memory.
+ *
+ * When GPU memory runs short, a sequence can be preempted by evicting its
+ * physical blocks to CPU memory and bringing them back later; the transfer
+ * is bound by the host link (0h-n0.github.io explainer, section
+ * "プリエンプション戦略", strategy 1).  This call performs such a transfer for
+ * a batch of blocks, in either direction; the host block manager keeps the
+ * mapping (BlockManager.swap_out / swap_in in the Python package).
+ *
+ * For every pair p < num_pairs with (s, d) = (block_pairs[2p], block_pairs[2p+1]):
+ *     dst_k[d][:][:][:] = src_k[s][:][:][:]   (all kv heads, all rows)
+ *     dst_v[d][:][:][:] = src_v[s][:][:][:]
+ * bitwise.  Swap-out: src = device pool, dst = host pool; swap-in: the
+ * reverse.  Pairs with s outside [0, src_num_blocks) or d outside
+ * [0, dst_num_blocks) are skipped.  Destinations must be distinct.
+ *   src_k, src_v, dst_k, dst_v   pools [blocks][num_kv_heads][block_size][head_dim]
+ *                in kv_dtype, 16-byte aligned.  A host pool must be pinned
+ *                memory that the device can address (hipHostMalloc; torch's
+ *                pin_memory=True): the GPU reads or writes it directly over
+ *                the host link, one kernel for the whole batch.
+ *   block_pairs  [num_pairs][2] int64, device (or pinned host) memory.
+ * num_pairs == 0 is a valid no-op.  Before launching, each pool pointer is
+ * checked with hipPointerGetAttributes: memory that is neither device memory
+ * nor pinned host memory mapped for the device returns PA_ERR_MEMORY.  The
+ * call is asynchronous on `stream`; synchronise before the host reads a
+ * swapped-out block.
+ */
+int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int64_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int src_num_blocks, int dst_num_blocks, int kv_dtype, void* stream);
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs.

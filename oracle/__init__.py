@@ -15,7 +15,9 @@ What it computes, and the passage each function follows:
   "KV量子化: FP8とINT8" (one byte per element; a scale is needed).
 * ``paging``    -- the physical pool ``[num_blocks][H_kv][B][d]``, the scatter
   of new tokens through a slot mapping, the block copy used by copy-on-write,
-  and the gather of a sequence's logical K/V through its block table
+  the block transfer between pools of preemption by swapping (section
+  "プリエンプション戦略" of the explainer below), and the gather of a
+  sequence's logical K/V through its block table
   (0h-n0.github.io, "論文解説: Efficient Memory Management for Large Language
   Model Serving with PagedAttention", sections "PagedAttentionのメモリ管理"
   and "Copy-on-Write（CoW）によるメモリ共有"; dihengye.cn, "PagedAttention",
@@ -46,4 +48,10 @@ from .attention import (  # noqa: F401
     split_kv_attention,
 )
 from .formats import decode_elements, e4m3fn_encode, e4m3fn_table, quantize_to_e4m3fn  # noqa: F401
-from .paging import copy_blocks, gather_sequence, quantize_reshape_and_cache, reshape_and_cache  # noqa: F401
+from .paging import (  # noqa: F401
+    copy_blocks,
+    gather_sequence,
+    quantize_reshape_and_cache,
+    reshape_and_cache,
+    swap_blocks,
+)

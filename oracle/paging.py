@@ -69,6 +69,29 @@ def copy_blocks(k_cache, v_cache, block_pairs):
         v_cache[int(d)] = v_src[int(s)]
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs):
+    """Copy whole blocks from one pool into another: ``dst[d] = src[s]`` (K
+    and V, every head and row) for each pair ``(s, d)``.
+
+    This is the transfer of preemption by swapping (0h-n0.github.io
+    explainer, section "プリエンプション戦略", strategy 1): a preempted
+    sequence's physical blocks move to a pool in CPU memory and later back
+    into free GPU blocks; the block tables are remapped on the host.  Pairs
+    naming a block outside either pool are skipped (a reading: the same rule
+    as for slots).
+
+    Parity: pinned in the oracle tests by a round trip through a second pool
+    that restores every sequence's gathered contents, and by untouched
+    destination blocks staying unchanged.
+    """
+    pairs = np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    for s, d in pairs:
+        s, d = int(s), int(d)
+        if 0 <= s < src_k.shape[0] and 0 <= d < dst_k.shape[0]:
+            dst_k[d] = src_k[s]
+            dst_v[d] = src_v[s]
+
+
 def gather_sequence(cache, table_row, seq_len, block_size):
     """Logical rows ``[H_kv][seq_len][d]`` of one sequence, via its table row.
 

@@ -90,6 +90,24 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, kv_dtype=None, stream=None):
         "pa_copy_blocks")
 
 
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, kv_dtype=None, stream=None):
+    """Copy whole blocks ``src[s] -> dst[d]`` for each ``(s, d)`` row of
+    ``block_pairs`` between two pools, one of them in pinned host memory
+    (swap-out: device -> host; swap-in: host -> device)."""
+    src_blocks, num_kv_heads, block_size, head_dim = src_k.shape
+    dst_blocks = dst_k.shape[0]
+    if tuple(dst_k.shape[1:]) != (num_kv_heads, block_size, head_dim):
+        raise ValueError("source and destination pools differ in block shape")
+    for t in (src_k, src_v, dst_k, dst_v):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("pa_swap_blocks: host pools must be pinned memory (pin_memory=True)")
+    device = src_k.device if src_k.is_cuda else dst_k.device
+    _check(_lib.load().pa_swap_blocks(
+        _ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(block_pairs), int(block_pairs.numel() // 2),
+        num_kv_heads, head_dim, block_size, src_blocks, dst_blocks, dtype_code(src_k, kv_dtype),
+        _stream(stream, device)), "pa_swap_blocks")
+
+
 def pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partition_size) -> int:
     return int(_lib.load().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_seq_len, partition_size))
 

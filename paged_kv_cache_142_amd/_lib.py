@@ -24,6 +24,8 @@ SIGNATURES = {
     "pa_reshape_and_cache_fp8": (_c_int, [_vp, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                           _c_int, _c_int, _vp]),
     "pa_copy_blocks": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "pa_swap_blocks": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _vp]),
     "pa_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pa_decode": (_c_int, _DECODE_ARGS),
     "pa_decode_partition": (_c_int, _DECODE_ARGS),

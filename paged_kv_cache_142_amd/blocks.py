@@ -16,6 +16,14 @@ Forked sequences (parallel samples, beams) share every block of their parent
 sequence drops its references and returns a block to the free list only when
 no other sequence still uses it (auturnal.com, "メモリ予算内での言語モデルの
 サービング", section 8).
+
+Preemption by swapping (explainer, section "プリエンプション戦略", strategy 1):
+``swap_out`` moves a sequence's blocks to a second pool of CPU blocks and
+frees its GPU blocks; ``swap_in`` brings them back into free GPU blocks.
+Both return the ``(source, destination)`` block pairs that
+``pa_swap_blocks`` transfers.  Only sequences that share no block can be
+swapped here (a shared block would have to stay where its other users read
+it).
 """
 
 from __future__ import annotations
@@ -28,9 +36,10 @@ class PoolExhausted(RuntimeError):
 
 
 class BlockManager:
-    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, free_order=None, num_cpu_blocks: int = 0):
         """``free_order``: the order in which free blocks are handed out
-        (default ascending ids)."""
+        (default ascending ids).  ``num_cpu_blocks``: size of the CPU pool
+        that swapped-out sequences occupy."""
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
         order = list(range(self.num_blocks)) if free_order is None else [int(b) for b in free_order]
@@ -41,6 +50,9 @@ class BlockManager:
         self._tables = {}
         self._lens = {}
         self._next_seq = 0
+        self.num_cpu_blocks = int(num_cpu_blocks)
+        self._cpu_free = deque(range(self.num_cpu_blocks))
+        self._swapped = {}  # seq -> CPU block table
 
     # ------------------------------------------------------------ blocks
     def allocate(self) -> int:
@@ -127,10 +139,47 @@ class BlockManager:
         return block * self.block_size + pos % self.block_size, pair
 
     def free_sequence(self, seq: int):
-        """Drop the sequence and its references (shared blocks stay alive)."""
-        for b in self._tables.pop(seq):
-            self._release(b)
+        """Drop the sequence and its references (shared blocks stay alive);
+        a swapped-out sequence returns its CPU blocks."""
+        if seq in self._swapped:
+            self._cpu_free.extend(self._swapped.pop(seq))
+        else:
+            for b in self._tables.pop(seq):
+                self._release(b)
         del self._lens[seq]
+
+    # ---------------------------------------------------------- swapping
+    def swap_out(self, seq: int):
+        """Move the sequence to CPU blocks.  Returns the ``(gpu, cpu)`` pairs
+        to transfer (device pool -> host pool); its GPU blocks are free
+        afterwards and the sequence has no table until ``swap_in``."""
+        table = self._tables[seq]
+        if any(self._ref[b] != 1 for b in table):
+            raise RuntimeError(f"sequence {seq} shares blocks and cannot be swapped out alone")
+        if len(self._cpu_free) < len(table):
+            raise PoolExhausted("no free CPU block")
+        cpu = [self._cpu_free.popleft() for _ in table]
+        pairs = list(zip(table, cpu))
+        for b in table:
+            self._release(b)
+        del self._tables[seq]
+        self._swapped[seq] = cpu
+        return pairs
+
+    def swap_in(self, seq: int):
+        """Bring a swapped-out sequence back into free GPU blocks.  Returns the
+        ``(cpu, gpu)`` pairs to transfer (host pool -> device pool)."""
+        cpu = self._swapped[seq]
+        if len(self._free) < len(cpu):
+            raise PoolExhausted("no free KV block")
+        gpu = [self.allocate() for _ in cpu]
+        del self._swapped[seq]
+        self._cpu_free.extend(cpu)
+        self._tables[seq] = gpu
+        return list(zip(cpu, gpu))
+
+    def is_swapped(self, seq: int) -> bool:
+        return seq in self._swapped
 
     def tables_array(self, seqs, width=None):
         """int32 ``[len(seqs)][width]`` block tables padded with -1."""
@@ -159,3 +208,7 @@ class BlockManager:
                 raise AssertionError(f"block {b} is free but referenced")
         if len(free) + sum(1 for r in self._ref if r > 0) != self.num_blocks:
             raise AssertionError("a block is neither free nor referenced")
+        held = [b for t in self._swapped.values() for b in t]
+        if len(set(held)) != len(held) or set(held) & set(self._cpu_free) or \
+                len(held) + len(self._cpu_free) != self.num_cpu_blocks:
+            raise AssertionError("CPU blocks are not partitioned into held and free")

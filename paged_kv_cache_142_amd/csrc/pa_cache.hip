@@ -1,7 +1,9 @@
 // KV-cache maintenance kernels for gfx950: the slot scatter of new tokens
-// (pa_reshape_and_cache) and the whole-block copy used by copy-on-write
-// (pa_copy_blocks).  Both move stored elements as 16-byte granules, so they
-// are bitwise and independent of the element format.
+// (pa_reshape_and_cache, and the quantizing pa_reshape_and_cache_fp8) and
+// the whole-block copy used by copy-on-write (pa_copy_blocks) and by
+// swapping between the device pool and a pinned host pool (pa_swap_blocks).
+// The scatter and the copies move stored elements as 16-byte granules, so
+// they are bitwise and independent of the element format.
 //
 // Pool layout: cache[num_blocks][num_kv_heads][block_size][head_dim]; one
 // token row of one head is head_dim * elem_bytes contiguous bytes (64..512,
@@ -42,18 +44,21 @@ reshape_and_cache_kernel(const u32x4* __restrict__ key, const u32x4* __restrict_
 }
 
 // grid.y = pair, grid.z = K|V; each thread copies one 16-byte granule of
-// the whole (all heads, all rows) block.
+// the whole (all heads, all rows) block from the source pool to the
+// destination pool (the same pool for copy-on-write; device and pinned host
+// memory for swapping).
 __global__ void __launch_bounds__(256)
-copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+copy_blocks_kernel(const u32x4* src_k, const u32x4* src_v, u32x4* dst_k, u32x4* dst_v,
                    const int64_t* __restrict__ block_pairs, int granules_per_block,
-                   int64_t num_blocks) {
+                   int64_t src_blocks, int64_t dst_blocks) {
     const int g = blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= granules_per_block) return;
     const int64_t src = block_pairs[2 * (int64_t)blockIdx.y];
     const int64_t dst = block_pairs[2 * (int64_t)blockIdx.y + 1];
-    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-    u32x4* cache = blockIdx.z == 0 ? k_cache : v_cache;
-    cache[dst * granules_per_block + g] = cache[src * granules_per_block + g];
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+    const u32x4* from = blockIdx.z == 0 ? src_k : src_v;
+    u32x4* to = blockIdx.z == 0 ? dst_k : dst_v;
+    to[dst * granules_per_block + g] = from[src * granules_per_block + g];
 }
 
 // Quantize-on-write: one thread per 16 output codes (16 elements of one
@@ -140,6 +145,7 @@ extern "C" const char* pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or GQA group not built";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
         case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+        case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pool is neither device memory nor pinned host memory the device can address";
         default: return "unknown pa_status";
     }
 }
@@ -200,22 +206,64 @@ extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, int 
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
-                              int num_pairs, int num_kv_heads, int head_dim, int block_size,
-                              int num_blocks, int kv_dtype, void* stream) {
-    using namespace pa;
+namespace pa {
+static int launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int64_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                              int block_size, int src_blocks, int dst_blocks, int kv_dtype, void* stream) {
     if (!valid_kv_dtype(kv_dtype)) return PA_ERR_DTYPE;
-    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || head_dim <= 0 || block_size <= 0)
+    if (num_pairs < 0 || num_kv_heads <= 0 || src_blocks <= 0 || dst_blocks <= 0 || head_dim <= 0 ||
+        block_size <= 0)
         return PA_ERR_SHAPE;
     if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
     if (num_pairs == 0) return PA_OK;
-    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+    if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs) return PA_ERR_NULL;
+    if (((uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)dst_k | (uintptr_t)dst_v) & 15u) return PA_ERR_SHAPE;
     if (num_pairs > 65535) return PA_ERR_SHAPE;
     const int64_t granules = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype) / 16;
     if (granules > 0x7fffffffLL) return PA_ERR_SHAPE;
     const unsigned gx = (unsigned)((granules + 255) / 256);
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0,
-                       (hipStream_t)stream, (u32x4*)k_cache, (u32x4*)v_cache, block_pairs,
-                       (int)granules, (int64_t)num_blocks);
+                       (hipStream_t)stream, (const u32x4*)src_k, (const u32x4*)src_v, (u32x4*)dst_k,
+                       (u32x4*)dst_v, block_pairs, (int)granules, (int64_t)src_blocks, (int64_t)dst_blocks);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+}  // namespace pa
+
+extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                              int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, int kv_dtype, void* stream) {
+    return pa::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, num_kv_heads,
+                                  head_dim, block_size, num_blocks, num_blocks, kv_dtype, stream);
+}
+
+namespace pa {
+// True when kernels may dereference p: device memory, or pinned host memory
+// mapped for the device at the same address.
+static bool device_addressable(const void* p) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+        return false;
+    }
+    if (attr.type == hipMemoryTypeDevice) return true;
+    if (attr.type == hipMemoryTypeHost) return attr.devicePointer == p;
+    return false;
+}
+}  // namespace pa
+
+extern "C" int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int64_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
+                              int block_size, int src_num_blocks, int dst_num_blocks, int kv_dtype,
+                              void* stream) {
+    // argument checks first (the same as for the launch), then the memory kinds
+    if (num_pairs > 0 && src_k && src_v && dst_k && dst_v && block_pairs && num_pairs <= 65535 &&
+        kv_dtype >= PA_DTYPE_F32 && kv_dtype <= PA_DTYPE_FP8_E4M3 && num_kv_heads > 0 && head_dim > 0 &&
+        block_size > 0 && src_num_blocks > 0 && dst_num_blocks > 0 &&
+        !(((uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)dst_k | (uintptr_t)dst_v) & 15u) &&
+        pa::supported_dim(head_dim) && pa::supported_block(block_size)) {
+        for (const void* p : {src_k, src_v, (const void*)dst_k, (const void*)dst_v, (const void*)block_pairs})
+            if (!pa::device_addressable(p)) return PA_ERR_MEMORY;
+    }
+    return pa::launch_copy_blocks(src_k, src_v, dst_k, dst_v, block_pairs, num_pairs, num_kv_heads, head_dim,
+                                  block_size, src_num_blocks, dst_num_blocks, kv_dtype, stream);
 }

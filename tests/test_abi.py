@@ -12,7 +12,7 @@ import pytest
 from paged_kv_cache_142_amd import _lib
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedattn.h")
-OK, NULL, SHAPE, DTYPE, UNSUP, WS, LAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, LAUNCH, MEMORY = 0, -1, -2, -3, -4, -5, -6, -7
 F32, F16, BF16, FP8 = 0, 1, 2, 3
 FAKE = 4096  # a non-null, 16-byte aligned address that validation never reaches
 
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, LAUNCH):
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, LAUNCH, MEMORY):
         assert lib.pa_status_string(code)
     assert b"unknown" in lib.pa_status_string(12345)
 
@@ -107,6 +107,30 @@ def test_copy_blocks_validation(lib):
     assert _cb(lib, dim=256) == UNSUP
     for ptr in ("k_cache", "v_cache", "pairs"):
         assert _cb(lib, **{ptr: None}) == NULL
+
+
+def _sw(lib, **kw):
+    a = dict(sk=FAKE, sv=FAKE, dk=FAKE, dv=FAKE, pairs=FAKE, n=3, heads=8, dim=128, block=16, sb=100, db=50,
+             dtype=BF16)
+    a.update(kw)
+    return lib.pa_swap_blocks(a["sk"], a["sv"], a["dk"], a["dv"], a["pairs"], a["n"], a["heads"], a["dim"],
+                              a["block"], a["sb"], a["db"], a["dtype"], None)
+
+
+def test_swap_blocks_validation(lib):
+    assert _sw(lib, n=0) == OK
+    assert _sw(lib, dtype=9) == DTYPE
+    assert _sw(lib, n=-1) == SHAPE
+    assert _sw(lib, sb=0) == SHAPE
+    assert _sw(lib, db=-4) == SHAPE
+    assert _sw(lib, n=70000) == SHAPE
+    assert _sw(lib, dk=FAKE + 8) == SHAPE  # not 16-byte aligned
+    assert _sw(lib, block=8) == UNSUP
+    for ptr in ("sk", "sv", "dk", "dv", "pairs"):
+        assert _sw(lib, **{ptr: None}) == NULL
+    # valid arguments, but the pools are not memory the GPU can address
+    # (no allocation lives at FAKE): refused before any launch
+    assert _sw(lib) == MEMORY
 
 
 def _dec(lib, fn="pa_decode", **kw):

@@ -156,3 +156,85 @@ def test_random_beam_workload_logical_contents_survive_cow():
         got = paging.gather_sequence(kc, bm.block_table(s), T, B)
         assert np.array_equal(got, logical[s].transpose(1, 0, 2))
         assert np.array_equal(paging.gather_sequence(vc, bm.block_table(s), T, B), -logical[s].transpose(1, 0, 2))
+
+
+# ------------------------------------------------------------- swapping
+
+def _filled(bm, lengths, rng):
+    """Sequences of the given lengths with random rows scattered into a
+    small float64 pool through the manager's slots."""
+    H, d = 2, 4
+    kc = np.full((bm.num_blocks, H, bm.block_size, d), np.nan)
+    vc = np.full_like(kc, np.nan)
+    seqs, rows = [], {}
+    for n in lengths:
+        s = bm.add_sequence()
+        slots = np.array([bm.append_slot(s)[0] for _ in range(n)], np.int64)
+        k, v = rng.standard_normal((n, H, d)), rng.standard_normal((n, H, d))
+        paging.reshape_and_cache(kc, vc, k, v, slots, bm.block_size)
+        seqs.append(s)
+        rows[s] = (k, v)
+    return kc, vc, seqs, rows
+
+
+def test_swap_out_and_in_restore_contents_and_counts():
+    """Preemption by swapping: a sequence's blocks move to the CPU pool
+    (its GPU blocks become free for others), then back into whatever GPU
+    blocks are free; the gathered logical rows are unchanged throughout."""
+    rng = np.random.default_rng(3)
+    bm = BlockManager(12, 4, free_order=rng.permutation(12), num_cpu_blocks=6)
+    kc, vc, seqs, rows = _filled(bm, [9, 5, 6], rng)
+    victim = seqs[0]
+    free_before = bm.num_free
+    out_pairs = bm.swap_out(victim)
+    assert len(out_pairs) == 3 and bm.is_swapped(victim) and bm.num_free == free_before + 3
+    bm.check_invariants()
+    ck = np.full((6,) + kc.shape[1:], np.nan)
+    cv = np.full_like(ck, np.nan)
+    paging.swap_blocks(kc, vc, ck, cv, out_pairs)
+    # the freed GPU blocks are reused and overwritten by another sequence
+    other = bm.add_sequence()
+    slots = np.array([bm.append_slot(other)[0] for _ in range(12)], np.int64)
+    paging.reshape_and_cache(kc, vc, np.zeros((12, 2, 4)), np.zeros((12, 2, 4)), slots, 4)
+    bm.free_sequence(other)
+    in_pairs = bm.swap_in(victim)
+    assert [c for c, _ in in_pairs] == [c for _, c in out_pairs]
+    paging.swap_blocks(ck, cv, kc, vc, in_pairs)
+    bm.check_invariants()
+    for s in seqs:
+        k, v = rows[s]
+        got_k = paging.gather_sequence(kc, bm.block_table(s), bm.seq_len(s), 4)
+        got_v = paging.gather_sequence(vc, bm.block_table(s), bm.seq_len(s), 4)
+        assert np.array_equal(got_k, k.transpose(1, 0, 2)) and np.array_equal(got_v, v.transpose(1, 0, 2))
+
+
+def test_swap_refuses_shared_blocks_and_exhaustion():
+    bm = BlockManager(8, 4, num_cpu_blocks=2)
+    s = bm.add_sequence()
+    for _ in range(6):
+        bm.append_slot(s)
+    child = bm.fork(s, 1)[0]
+    with pytest.raises(RuntimeError):
+        bm.swap_out(s)
+    bm.free_sequence(child)
+    t = bm.add_sequence()
+    for _ in range(12):
+        bm.append_slot(t)
+    with pytest.raises(PoolExhausted):
+        bm.swap_out(t)  # three blocks, two CPU blocks
+    pairs = bm.swap_out(s)
+    assert len(pairs) == 2
+    bm.free_sequence(s)  # a swapped-out sequence returns its CPU blocks
+    bm.check_invariants()
+    assert bm.num_free == 8 - 3
+
+
+def test_swap_blocks_oracle_skips_out_of_range_and_leaves_the_rest():
+    src_k = np.arange(4 * 2 * 3, dtype=np.float64).reshape(4, 2, 3)
+    src_v = -src_k
+    dst_k = np.full((3, 2, 3), 7.0)
+    dst_v = np.full((3, 2, 3), 8.0)
+    paging.swap_blocks(src_k, src_v, dst_k, dst_v, [[2, 0], [5, 1], [1, 7], [-1, 2], [3, 2]])
+    assert np.array_equal(dst_k[0], src_k[2]) and np.array_equal(dst_v[0], src_v[2])
+    assert np.array_equal(dst_k[2], src_k[3]) and np.array_equal(dst_v[2], src_v[3])
+    assert np.all(dst_k[1] == 7.0) and np.all(dst_v[1] == 8.0)

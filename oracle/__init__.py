@@ -28,6 +28,11 @@ What it computes, and the passage each function follows:
   auturnal.com, "メモリ予算内での言語モデルのサービング", equation (4), and
   the log-sum-exp merge of per-partition partial states that the same
   recurrence implies.
+* ``prefill``   -- multi-query (prefill / chunked prefill) attention over the
+  same paged K/V: each new token's query attends causally to the cached
+  tokens up to its own position (the explainer's attention definition,
+  restricted; auturnal.com review, sections 1 and 7, on prefill versus
+  decode shapes).
 * ``accounting`` -- KV bytes per token (equation (1) of the auturnal.com
   review; youngju.dev section "KVキャッシュはなぜメモリを消費するのか"),
   page-tail waste and its bound (equation (2)), the exact mean tail waste for
@@ -38,7 +43,7 @@ function is listed in its docstring; all are pinned by ``tests/test_oracle*.py``
 against closed forms, printed worked examples, library routines or brute force.
 """
 
-from . import accounting, attention, formats, paging  # noqa: F401
+from . import accounting, attention, formats, paging, prefill  # noqa: F401
 from .attention import (  # noqa: F401
     dense_attention,
     lse_merge,
@@ -47,6 +52,7 @@ from .attention import (  # noqa: F401
     paged_decode_row,
     split_kv_attention,
 )
+from .prefill import paged_prefill, paged_prefill_rowwise  # noqa: F401
 from .formats import decode_elements, e4m3fn_encode, e4m3fn_table, quantize_to_e4m3fn  # noqa: F401
 from .paging import (  # noqa: F401
     copy_blocks,

@@ -15,15 +15,22 @@ measure on (the pages' datasets are not used):
 * ``mha``            -- fp16, 256 sequences, lengths uniform on 1..2048, 40/40 heads
 * ``shared_prefix``  -- bf16, 8 prompts x 6 beams sharing the prompt's blocks
 * ``long_fp8``       -- fp8 E4M3 KV with per-kv-head scales, 16 x 32768 tokens, 64/8 heads
+
+and, for multi-query attention over the same pool, ``prefill`` -- bf16,
+16 sequences of 1..2048 tokens, 32/8 heads, every token (or the last chunk of
+each sequence) a query.
 """
 
 from .generators import (  # noqa: F401
     DecodeWorkload,
+    PrefillWorkload,
     SharedPrefixWorkload,
+    build_prefill_workload,
     gqa,
     long_fp8,
     make,
     mha,
+    prefill,
     shared_prefix,
     tiny,
 )

@@ -351,7 +351,76 @@ def shared_prefix(seed=0, prompt_len=1032, num_prompts=8, beams=6, max_suffix=25
         suffix_values=suffix_values, q=q, extreme=extreme, logit_target=logit_target)
 
 
+@dataclass
+class PrefillWorkload:
+    """A multi-query (prefill) step over paged K/V.
+
+    ``cache`` holds every sequence's ``T_i = cache.seq_lens[i]`` tokens (its
+    keys, values, block tables and slots); the step's query rows are the last
+    ``query_lens[i]`` tokens of each sequence, packed: sequence ``i`` owns rows
+    ``query_start[i] .. query_start[i+1] - 1`` of ``q`` (raw ``[total_q][H][d]``).
+    Before the step the cache holds each sequence's earlier tokens; the step
+    writes the chunk's keys and values, then attends.
+    """
+    cache: DecodeWorkload
+    query_lens: np.ndarray   # int32 [N]
+    query_start: np.ndarray  # int32 [N+1]
+    q: np.ndarray            # raw [total_q][H][d]
+
+    @property
+    def name(self):
+        return self.cache.name
+
+    @property
+    def total_q(self):
+        return int(self.query_start[-1])
+
+    def chunk_rows(self):
+        """Rows of ``cache.keys`` written by the step (each sequence's last Q_i)."""
+        off = self.cache.token_offsets
+        return np.concatenate([np.arange(off[i + 1] - self.query_lens[i], off[i + 1], dtype=np.int64)
+                               for i in range(len(self.query_lens))]) if len(self.query_lens) else \
+            np.zeros(0, np.int64)
+
+    def context_rows(self):
+        """Rows cached before the step."""
+        keep = np.ones(len(self.cache.slots), dtype=bool)
+        keep[self.chunk_rows()] = False
+        return np.nonzero(keep)[0]
+
+
+def build_prefill_workload(name, seed, *, seq_lens, query_lens, num_heads, num_kv_heads, head_dim, block_size,
+                           kv_dtype, q_dtype, spare_blocks=0):
+    """Assemble a ``PrefillWorkload``: the cache as for decode (seeded), plus
+    N(0, 1) query rows for each sequence's last ``query_lens[i]`` tokens."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    query_lens = np.asarray(query_lens, dtype=np.int32)
+    if np.any(query_lens < 0) or np.any(query_lens > seq_lens):
+        raise ValueError("query_lens must lie in [0, seq_lens]")
+    cache = build_decode_workload(name, seed, seq_lens=seq_lens, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                                  head_dim=head_dim, block_size=block_size, kv_dtype=kv_dtype, q_dtype=q_dtype,
+                                  spare_blocks=spare_blocks, num_copy_pairs=0, partition_size=512)
+    start = np.zeros(len(query_lens) + 1, dtype=np.int32)
+    start[1:] = np.cumsum(query_lens)
+    rng = np.random.default_rng(_seed(seed, 20))
+    q = round_to_storage(rng.standard_normal((int(start[-1]), num_heads, head_dim), dtype=np.float32), q_dtype)
+    return PrefillWorkload(cache=cache, query_lens=query_lens, query_start=start, q=q)
+
+
+def prefill(seed=0, num_seqs=16, max_len=2048, chunk=None, kv_dtype="bf16", num_heads=32, num_kv_heads=8,
+            head_dim=128, block_size=16):
+    """bf16, 32/8 heads, d=128, B=16, context lengths uniform on 1..max_len;
+    full prefill (every token a query) or, with ``chunk``, the last
+    ``min(chunk, T)`` tokens of each sequence."""
+    lens = np.random.default_rng(_seed(seed, 21)).integers(1, max_len + 1, size=num_seqs)
+    qlens = lens if chunk is None else np.minimum(lens, chunk)
+    return build_prefill_workload(f"prefill{'' if chunk is None else f'_chunk{chunk}'}", seed, seq_lens=lens,
+                                  query_lens=qlens, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                                  head_dim=head_dim, block_size=block_size, kv_dtype=kv_dtype,
+                                  q_dtype="bf16" if kv_dtype == "fp8_e4m3" else kv_dtype)
+
+
 def make(name, seed=0, **kw):
-    """Workload by name: tiny, gqa, mha, shared_prefix, long_fp8."""
+    """Workload by name: tiny, gqa, mha, shared_prefix, long_fp8, prefill."""
     return {"tiny": tiny, "gqa": gqa, "mha": mha, "shared_prefix": shared_prefix,
-            "long_fp8": long_fp8}[name](seed=seed, **kw)
+            "long_fp8": long_fp8, "prefill": prefill}[name](seed=seed, **kw)

@@ -266,6 +266,50 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
                      int num_blocks, float scale, const float* k_scale, const float* v_scale,
                      int partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_prefill -- multi-query (prefill or chunked prefill) attention over the
+ * same paged K/V.
+ *
+ * A prefill step attends for many new tokens of a sequence at once; its
+ * computational shape differs from a decode step's (auturnal.com, "メモリ予
+ * 算内での言語モデルのサービング", section 7).  The new tokens' keys and values
+ * are first written into the sequence's blocks (pa_reshape_and_cache); then
+ * each new token's query attends to the cached tokens up to its own position.
+ * For sequence i with T = seq_lens[i] and Q = query_start[i+1] -
+ * query_start[i], packed query row r = query_start[i] + j (j < Q) sits at
+ * position p = T - Q + j, and for query head h (kv head h / G):
+ *     out[r][h][:] = softmax(scale * K_i[0..p] q[r][h]) V_i[0..p]
+ * (0h-n0.github.io explainer, section "Attention計算", restricted to the keys
+ * up to p).  Q == T is a full prefill, Q < T a chunk appended to a context.
+ *
+ * Method: one workgroup per (sequence, tile of 64/G query tokens, kv head);
+ * the tile's 64 (token, head) columns share each staged 32-key K/V step, and
+ * the score and value products run on the matrix cores (v_mfma_f32_16x16x32,
+ * fp32 accumulation; softmax weights enter the value product as a 16-bit
+ * high part plus remainder) with the online-softmax recurrence of equation
+ * (4) of the same review per column.
+ *
+ *   out          [total_q][num_heads][head_dim], out_dtype (F32, F16 or BF16)
+ *   q            [total_q][num_heads][head_dim], q_dtype, 16-byte aligned
+ *   query_start  [num_seqs + 1] int32, device; non-decreasing, last = total_q
+ *   max_query_len  host upper bound of the per-sequence query counts (sizes
+ *                the grid); at most max_seq_len
+ *   k_cache, v_cache, block_tables, max_blocks_per_seq, seq_lens,
+ *   max_seq_len, num_blocks, scale: as for pa_decode.
+ * Rows of a sequence whose length is invalid (0, above max_seq_len, needing
+ * more than max_blocks_per_seq blocks, or shorter than its query count), or
+ * whose table names a block outside the pool, are NaN.
+ *
+ * Supported: head_dim 128; block_size 16 or 32; G in {1, 2, 4, 8};
+ * (kv_dtype, q_dtype) = (BF16, BF16) or (F16, F16); other valid formats return
+ * PA_ERR_UNSUPPORTED.  total_q == 0 is a valid no-op.
+ */
+int pa_prefill(void* out, int out_dtype, const void* q, int q_dtype, const int32_t* query_start,
+               int total_q, int max_query_len, const void* k_cache, const void* v_cache, int kv_dtype,
+               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* seq_lens,
+               int max_seq_len, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+               int block_size, int num_blocks, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,6 +124,25 @@ def _decode_argv(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, 
             _stream(stream, q.device))
 
 
+def _prefill_argv(out, q, query_start, k_cache, v_cache, block_tables, seq_lens, max_seq_len, max_query_len,
+                  scale, kv_dtype=None, q_dtype=None, out_dtype=None, stream=None):
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    total_q, num_heads, _ = q.shape
+    return (_ptr(out), dtype_code(out, out_dtype), _ptr(q), dtype_code(q, q_dtype), _ptr(query_start), total_q,
+            int(max_query_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache, kv_dtype), _ptr(block_tables),
+            int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(seq_lens.numel()), num_heads,
+            num_kv_heads, head_dim, block_size, num_blocks, float(scale), _stream(stream, q.device))
+
+
+def pa_prefill(*args, **kw):
+    """Causal multi-query attention of packed query rows over paged K/V.
+
+    Arguments: ``out, q, query_start, k_cache, v_cache, block_tables,
+    seq_lens, max_seq_len, max_query_len, scale``; see ``include/pagedattn.h``.
+    """
+    _check(_lib.load().pa_prefill(*_prefill_argv(*args, **kw)), "pa_prefill")
+
+
 def prepared(name, *args, **kw):
     """A zero-argument callable that issues the C call ``name`` with these
     arguments, marshalled once (for loops that repeat an identical call).
@@ -134,6 +153,8 @@ def prepared(name, *args, **kw):
     fn = getattr(lib, name)
     if name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
         argv = _decode_argv(*args, **kw)
+    elif name == "pa_prefill":
+        argv = _prefill_argv(*args, **kw)
     elif name == "pa_reshape_and_cache":
         key, value, k_cache, v_cache, slot_mapping = args
         nb, hkv, bs, d = k_cache.shape

@@ -27,6 +27,8 @@ SIGNATURES = {
     "pa_swap_blocks": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 _vp]),
     "pa_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pa_prefill": (_c_int, [_vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp,
+                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
     "pa_decode": (_c_int, _DECODE_ARGS),
     "pa_decode_partition": (_c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c_int, _DECODE_ARGS),

@@ -170,3 +170,31 @@ def test_decode_validation(lib, fn):
     assert _dec(lib, fn, q=FAKE + 4) == SHAPE             # misaligned
     need = lib.pa_decode_workspace_size(64, 32, 128, 4096, 512)
     assert _dec(lib, fn, ws_bytes=need - 1) == WS
+
+
+def _pf(lib, **kw):
+    a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, qs=FAKE, total_q=100, mql=64, kc=FAKE, vc=FAKE,
+             kv=BF16, bt=FAKE, mbps=64, lens=FAKE, msl=1024, n=4, heads=32, kvh=8, dim=128, block=16, blocks=500,
+             scale=0.1)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["qs"], a["total_q"], a["mql"],
+                          a["kc"], a["vc"], a["kv"], a["bt"], a["mbps"], a["lens"], a["msl"], a["n"], a["heads"],
+                          a["kvh"], a["dim"], a["block"], a["blocks"], a["scale"], None)
+
+
+def test_prefill_validation(lib):
+    assert _pf(lib, total_q=0) == OK
+    assert _pf(lib, n=0) == OK
+    assert _pf(lib, kv=7) == DTYPE
+    assert _pf(lib, out_dtype=FP8) == DTYPE
+    assert _pf(lib, n=-1) == SHAPE
+    assert _pf(lib, heads=30) == SHAPE          # not a multiple of the kv heads
+    assert _pf(lib, mql=2000) == SHAPE          # more queries than the longest sequence
+    assert _pf(lib, mbps=10) == SHAPE           # table rows too short for max_seq_len
+    assert _pf(lib, kv=FP8) == UNSUP            # valid format, not built for prefill
+    assert _pf(lib, kv=F32, q_dtype=F32) == UNSUP
+    assert _pf(lib, dim=64) == UNSUP
+    assert _pf(lib, heads=48, kvh=3) == UNSUP   # group 16
+    for ptr in ("out", "q", "qs", "kc", "vc", "bt", "lens"):
+        assert _pf(lib, **{ptr: None}) == NULL
+    assert _pf(lib, q=FAKE + 4) == SHAPE        # not 16-byte aligned

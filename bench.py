@@ -46,7 +46,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="gqa",
-                   choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow"])
+                   choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow",
+                            "prefill", "prefill_chunk"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -169,6 +170,93 @@ def swap_bandwidth(mib, steps):
                       "swap_out_GBs": round(byts / times["out"] / 1e9, 2),
                       "swap_in_GBs": round(byts / times["in"] / 1e9, 2),
                       "swap_out_ms": round(times["out"] * 1e3, 3), "swap_in_ms": round(times["in"] * 1e3, 3)}))
+
+
+def prefill_flops(wl):
+    """Algorithmic flops of one prefill step: for every query row at position
+    p and query head, 2 d for the scores and 2 d for the values against each
+    of the p + 1 keys it may see."""
+    c = wl.cache
+    total = 0
+    for T, Q in zip(c.seq_lens.astype(np.int64), wl.query_lens.astype(np.int64)):
+        first = T - Q + 1  # keys seen by the first query row
+        total += (first + T) * Q // 2
+    return int(total) * c.num_heads * 4 * c.head_dim
+
+
+def run_prefill(args):
+    """The prefill step: scatter of the chunk tokens' K/V, then pa_prefill."""
+    import torch
+    import paged_kv_cache_142_amd as pa
+    import workloads
+    chunk = None if args.config == "prefill" else 512
+    wl = workloads.prefill(args.seed, chunk=chunk)
+    c = wl.cache
+    view = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+    def up(raw, fmt):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(view[fmt]).cuda()
+
+    kc = torch.zeros(c.pool_shape(), dtype=view[c.kv_dtype], device="cuda")
+    vc = torch.zeros_like(kc)
+    keys, values = up(c.keys, c.kv_dtype), up(c.values, c.kv_dtype)
+    slots = torch.from_numpy(c.slots).cuda()
+    ctx = torch.from_numpy(wl.context_rows()).cuda()
+    if len(ctx):
+        pa.pa_reshape_and_cache(keys[ctx].contiguous(), values[ctx].contiguous(), kc, vc, slots[ctx].contiguous())
+    ch = torch.from_numpy(wl.chunk_rows()).cuda()
+    ck, cv, cs = keys[ch].contiguous(), values[ch].contiguous(), slots[ch].contiguous()
+    del keys, values
+    q = up(wl.q, c.q_dtype)
+    out = torch.empty((wl.total_q, c.num_heads, c.head_dim), dtype=torch.float32, device="cuda")
+    qs = torch.from_numpy(wl.query_start).cuda()
+    tables = torch.from_numpy(c.block_tables).cuda()
+    lens = torch.from_numpy(c.seq_lens).cuda()
+    calls = [pa.prepared("pa_reshape_and_cache", ck, cv, kc, vc, cs),
+             pa.prepared("pa_prefill", out, q, qs, kc, vc, tables, lens, c.max_seq_len, int(wl.query_lens.max()),
+                         float(c.scale))]
+    for _ in range(args.warmup):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        for call in calls:
+            call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record()
+        calls[0]()
+        e[1].record()
+        calls[1]()
+        e[2].record()
+    torch.cuda.synchronize()
+    scatter_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    prefill_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    flops = prefill_flops(wl)
+    tflops = flops / (prefill_us * 1e-6) / 1e12
+    line = {
+        "metric": "paged prefill attn: algorithmic TFLOP/s (causal), query tokens/s",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {c.num_seqs} seqs, sum T={int(c.seq_lens.sum())} (max {c.max_seq_len}), "
+                               f"{wl.total_q} query tokens, {c.num_heads}/{c.num_kv_heads} heads, d={c.head_dim}, "
+                               f"B={c.block_size}, {c.kv_dtype} K/V/q, f32 out; step = scatter of the query "
+                               f"tokens' K/V + pa_prefill", "seed": wl.cache.seed,
+                   "flops_per_step": flops, "query_tokens": wl.total_q},
+        "query_tokens_per_s": round(wl.total_q / (ms * 1e-3), 1),
+        "kernels_us": {"reshape_and_cache": round(scatter_us, 2), "prefill": round(prefill_us, 2)},
+        "roofline": {"kernel": "pa_prefill", "bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "note": "bf16 dense matrix-core peak; the kernel issues 1.5x the algorithmic flops "
+                             "(hi/lo halves of p) and computes masked keys of the diagonal steps"},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def _workload(name, seed, partition_size):
@@ -389,6 +477,9 @@ def main():
         return
     if args.swap_mib:
         swap_bandwidth(args.swap_mib, args.steps)
+        return
+    if args.config.startswith("prefill"):
+        run_prefill(args)
         return
     wl = _workload(args.config, args.seed, args.partition_size)
     if args.graph and args.pools != 1:

@@ -106,8 +106,13 @@ __device__ __forceinline__ float prefill_sum_groups(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 4
+#endif
+
 template <int D, int BS, int G>
 struct PrefillShape {
+    static constexpr int S = PA_PREFILL_STAGES;   // LDS stages (S - 1 steps of copies in flight)
     static constexpr int W = 4;                   // waves per workgroup
     static constexpr int COLS = 16;               // query columns per wave
     static constexpr int TQ = W * COLS / G;       // query tokens per workgroup
@@ -120,7 +125,7 @@ struct PrefillShape {
     static constexpr int COPIES = STAGE / 1024;   // 1 KiB copies per step
     static constexpr int COPIES_PER_WAVE = COPIES / W;
     static constexpr int ID_CAP = 2048;           // block ids held in LDS
-    static constexpr int IDS_AT = 2 * STAGE;
+    static constexpr int IDS_AT = S * STAGE;
     static constexpr int LDS = IDS_AT + ID_CAP * 4 + 16;
     static_assert(D == 128, "the lane roles assume head_dim 128");
     static_assert(BS == 16 || BS == 32, "block size");
@@ -128,6 +133,7 @@ struct PrefillShape {
     static_assert(COPIES % W == 0, "copies split evenly over the waves");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
+    static_assert(S >= 2 && S <= 4, "the waits below cover two to four stages");
 };
 
 template <Fmt KV, int D, int BS, int G>
@@ -350,24 +356,41 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
         }
     };
 
-    // ---- main loop over 32-key steps
+    // ---- main loop over 32-key steps, S - 1 steps of copies ahead.  The
+    // first S - 1 steps never need a new id window (S - 1 < ID_CAP / BPS).
+    constexpr int S = Sh::S;
     const int nsteps = pos_max / STEP + 1;
     const int steps_per_window = Sh::ID_CAP / BPS;
-    issue(0, 0);
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        if (k < nsteps) issue(k, k);
     for (int k = 0; k < nsteps; ++k) {
-        wait_vmcnt<0>();  // this wave's copies of step k
+        // this wave's copies of step k are complete when at most those of the
+        // later steps already issued (up to S - 2 of them) are in flight
+        const int later = min(S - 2, nsteps - 1 - k);
+        if constexpr (S >= 4) {
+            if (later >= 2) wait_vmcnt<2 * Sh::COPIES_PER_WAVE>();
+            else if (later == 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
+            else wait_vmcnt<0>();
+        } else if constexpr (S == 3) {
+            if (later >= 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __syncthreads();  // everyone's copies of step k landed; step k-1 is finished everywhere
-        if (k + 1 < nsteps) {
-            if ((k + 1) % steps_per_window == 0) {  // the next step's ids are in the next window
-                window = (k + 1) * BPS;
+        const int kn = k + S - 1;  // the step whose copies go out now, into step k-1's stage
+        if (kn < nsteps) {
+            if (kn % steps_per_window == 0) {  // its ids are in the next window
+                window = kn * BPS;
                 load_ids(window);
                 __syncthreads();
             }
-            issue(k + 1, (k + 1) & 1);
+            issue(kn, kn % S);
         }
         const int k0 = k * STEP;
         if (wave_cols && k0 <= wpos_max) {  // some column of this wave sees keys of this step
-            const char* st = smem + (k & 1) * Sh::STAGE;
+            const char* st = smem + (k % S) * Sh::STAGE;
             if (k0 + STEP - 1 <= wpos_min && k0 + STEP <= T)
                 step(st, k0, std::false_type{});
             else

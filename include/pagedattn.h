@@ -267,6 +267,47 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
                      int partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode for batches whose sequences share
+ * prompt blocks (parallel samples and beams forked from one prompt), reading
+ * each shared block once per group instead of once per sequence.
+ *
+ * Forked sequences share every block of their parent through reference
+ * counts (dihengye.cn, "PagedAttention", section "KV Cache 共享机制"; the
+ * explainer's section "Copy-on-Write（CoW）によるメモリ共有"), so their
+ * attention reads the same prompt K/V several times.  Here sequences
+ * group_start[g] .. group_start[g+1]-1 form group g, and the first
+ * group_prefix[g] tokens of every member are held in the same physical
+ * blocks (precondition: the members' tables name the same ids for those
+ * blocks; the group's first sequence's table is read).  The first
+ * floor(group_prefix[g] / partition_size) partitions of the members are
+ * computed once for the whole group on the matrix cores, with all members'
+ * queries together; the remaining partitions of every sequence run as in
+ * pa_decode and the same log-sum-exp merge combines them.  The result equals
+ * pa_decode's up to the order of floating-point operations.
+ *
+ *   group_start   [num_groups + 1] int32, device: non-decreasing, from 0 to
+ *                 num_seqs (otherwise results are undefined, without access
+ *                 outside the arguments)
+ *   group_prefix  [num_groups] int32, device: shared tokens of each group
+ *   max_group_size, max_prefix_len   host bounds that size the grid: members
+ *                 past the first max_group_size of a group are computed alone,
+ *                 and prefixes are shared up to max_prefix_len tokens
+ *   other arguments: as for pa_decode (same workspace size).
+ * A member holding fewer tokens than its group's shared partitions is
+ * computed alone; so is a whole group whose first sequence is that short.
+ * Shapes the matrix-core path does not cover (FP8 or F32 KV, head_dim 64,
+ * G = 16) and num_groups == 0 run pa_decode unchanged.
+ */
+int pa_decode_shared_prefix(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                            const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                            int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            float scale, const float* k_scale, const float* v_scale, int partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream, const int32_t* group_start,
+                            const int32_t* group_prefix, int num_groups, int max_group_size,
+                            int max_prefix_len);
+
+/*
  * pa_prefill -- multi-query (prefill or chunked prefill) attention over the
  * same paged K/V.
  *

@@ -153,6 +153,9 @@ def prepared(name, *args, **kw):
     fn = getattr(lib, name)
     if name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
         argv = _decode_argv(*args, **kw)
+    elif name == "pa_decode_shared_prefix":
+        gs, gp, mgs, mpl = (kw.pop(k) for k in ("group_start", "group_prefix", "max_group_size", "max_prefix_len"))
+        argv = _decode_argv(*args, **kw) + _group_argv(gs, gp, mgs, mpl)
     elif name == "pa_prefill":
         argv = _prefill_argv(*args, **kw)
     elif name == "pa_reshape_and_cache":
@@ -194,6 +197,25 @@ def pa_decode(*args, **kw):
     ``v_scale``; see ``include/pagedattn.h``.
     """
     _decode_call("pa_decode", *args, **kw)
+
+
+def pa_decode_shared_prefix(*args, group_start, group_prefix, max_group_size, max_prefix_len, **kw):
+    """``pa_decode`` reading each group's shared prompt partitions once.
+
+    ``group_start`` (int32, ``[G+1]``) and ``group_prefix`` (int32, ``[G]``
+    shared tokens) are device tensors; the other arguments are ``pa_decode``'s.
+    """
+    argv = _decode_argv(*args, **kw) + _group_argv(group_start, group_prefix, max_group_size, max_prefix_len)
+    _check(_lib.load().pa_decode_shared_prefix(*argv), "pa_decode_shared_prefix")
+
+
+def _group_argv(group_start, group_prefix, max_group_size, max_prefix_len):
+    if group_start.numel() != group_prefix.numel() + 1:
+        raise ValueError("group_start needs one entry more than group_prefix")
+    if group_start.dtype != torch.int32 or group_prefix.dtype != torch.int32:
+        raise ValueError("group_start and group_prefix must be int32")
+    return (_ptr(group_start), _ptr(group_prefix), int(group_prefix.numel()), int(max_group_size),
+            int(max_prefix_len))
 
 
 def pa_decode_partition(*args, **kw):

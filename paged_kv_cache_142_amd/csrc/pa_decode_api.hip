@@ -14,15 +14,19 @@ static int num_partitions(int max_seq_len, int partition_size) {
 }
 
 // Workspace: m[N][H][P_max] | l[N][H][P_max] | acc[N][H][P_max][D] (float32)
-// | plan (int32: count, then N * P_max work items), each part starting on a
+// | plan (int32: count, then N * P_max work items) | skipped partitions per
+// sequence (int32 [N], shared-prefix decode), each part starting on a
 // 256-byte boundary.
 static size_t plan_offset(int num_seqs, int num_heads, int head_dim, int max_parts) {
     const size_t rows = (size_t)num_seqs * num_heads * max_parts;
     return 2 * align256(rows * 4) + align256(rows * head_dim * 4);
 }
-static size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int max_parts) {
+static size_t skip_offset(int num_seqs, int num_heads, int head_dim, int max_parts) {
     return plan_offset(num_seqs, num_heads, head_dim, max_parts) +
-           4 * (PLAN_ITEMS_OFFSET + (size_t)num_seqs * max_parts);
+           align256(4 * (PLAN_ITEMS_OFFSET + (size_t)num_seqs * max_parts));
+}
+static size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int max_parts) {
+    return skip_offset(num_seqs, num_heads, head_dim, max_parts) + 4 * (size_t)num_seqs;
 }
 
 constexpr int PLAN_THREADS = 1024;
@@ -47,12 +51,16 @@ __global__ void __launch_bounds__(PLAN_THREADS) decode_plan_kernel(const DecodeA
     auto bucket = [&](int size) { return min(PB - size, NBK - 1); };  // 0 = full partitions
     for (int k = tid; k < PLAN_BUCKETS; k += PLAN_THREADS) hist[k] = 0;
     __syncthreads();
+    // items of sequence i: its partitions from skip_parts[i] on
+    auto first_part = [&](int i, int np) { return a.skip_parts ? min(max(a.skip_parts[i], 0), np) : 0; };
     for (int i = tid; i < a.num_seqs; i += PLAN_THREADS) {
         const int T = a.seq_lens[i];
         if (T <= 0 || T > a.max_seq_len || (T + B - 1) / B > a.max_blocks_per_seq) continue;
         const int np = (T + P - 1) / P;
         const int last = (T + B - 1) / B - (np - 1) * PB;
-        if (np > 1) atomicAdd(&hist[0], np - 1);
+        const int p0 = first_part(i, np);
+        if (p0 >= np) continue;
+        if (np - 1 > p0) atomicAdd(&hist[0], np - 1 - p0);
         atomicAdd(&hist[bucket(last)], 1);
     }
     __syncthreads();
@@ -72,7 +80,7 @@ __global__ void __launch_bounds__(PLAN_THREADS) decode_plan_kernel(const DecodeA
         if (T <= 0 || T > a.max_seq_len || (T + B - 1) / B > a.max_blocks_per_seq) continue;
         const int np = (T + P - 1) / P;
         const int last = (T + B - 1) / B - (np - 1) * PB;
-        for (int p = 0; p < np; ++p) {
+        for (int p = first_part(i, np); p < np; ++p) {
             const int pos = atomicAdd(&hist[bucket(p < np - 1 ? PB : last)], 1);
             a.plan[PLAN_ITEMS_OFFSET + pos] = i * a.max_partitions + p;
         }
@@ -291,11 +299,8 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.part_l = (float*)((char*)workspace + align256(rows * 4));
     a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
     a.plan = (int*)((char*)workspace + plan_offset(num_seqs, num_heads, head_dim, max_parts));
-#ifndef PA_NO_INLINE_PLAN
     a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
-#else
-    a.inline_plan = 0;
-#endif
+    a.skip_parts = nullptr;
     pr.head_dim = head_dim;
     pr.group = group;
     pr.kv_dtype = kv_dtype;
@@ -368,4 +373,30 @@ extern "C" int pa_decode(PA_DECODE_PARAMS) {
     const int s1 = pa::run_partition(pr, (hipStream_t)stream);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, (hipStream_t)stream);
+}
+
+extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_start, const int32_t* group_prefix,
+                                       int num_groups, int max_group_size, int max_prefix_len) {
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    if (num_groups < 0 || max_group_size < 0 || max_prefix_len < 0) return PA_ERR_SHAPE;
+    if (num_groups > 0 && (!group_start || !group_prefix)) return PA_ERR_NULL;
+    const hipStream_t s = (hipStream_t)stream;
+    // nothing to share, or a shape the matrix-core tile does not cover: plain decode
+    if (num_groups == 0 || max_prefix_len < partition_size || max_group_size == 0 ||
+        !pa::prefix_states_supported(pr.kv_dtype, pr.q_dtype, pr.head_dim, block_size, pr.group)) {
+        const int s1 = pa::run_partition(pr, s);
+        if (s1 != PA_OK) return s1;
+        return pa::run_reduce(pr, s);
+    }
+    int32_t* skip = (int32_t*)((char*)workspace + pa::skip_offset(num_seqs, num_heads, head_dim,
+                                                                  pr.args.max_partitions));
+    const int s0 = pa::launch_prefix_states(pr.args, pr.kv_dtype, pr.group, group_start, group_prefix, num_groups,
+                                            max_group_size, max_prefix_len, skip, s);
+    if (s0 != PA_OK) return s0;
+    pr.args.skip_parts = skip;
+    const int s1 = pa::run_partition(pr, s);
+    if (s1 != PA_OK) return s1;
+    return pa::run_reduce(pr, s);
 }

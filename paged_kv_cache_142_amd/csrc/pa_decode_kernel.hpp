@@ -70,6 +70,10 @@ struct DecodeArgs {
     // 1: no plan kernel ran; every partition workgroup derives its item from
     // seq_lens itself (at most 64 sequences and 64 blocks per partition).
     int inline_plan;
+    // Leading partitions of each sequence computed elsewhere (the shared
+    // prefix of its group, by the prefix kernel); nullptr: none.  Those
+    // partitions have no items here; their states are in the workspace.
+    const int32_t* skip_parts;
 };
 
 constexpr int PLAN_ITEMS_OFFSET = 64;
@@ -102,20 +106,26 @@ __device__ __forceinline__ bool inline_plan_item(const DecodeArgs& a, int k, int
     const int P = a.partition_size;
     const int PB = P / B;
     const int T = lane < a.num_seqs ? a.seq_lens[lane] : 0;
+    const int skip = (a.skip_parts && lane < a.num_seqs) ? a.skip_parts[lane] : 0;
     const bool ok = T > 0 && T <= a.max_seq_len && (T + B - 1) / B <= a.max_blocks_per_seq;
     const int np = ok ? (T + P - 1) / P : 0;
     const int rem = ok ? (T + B - 1) / B - (np - 1) * PB : 0;  // blocks of the last partition
-    const int nfull = ok ? np - (rem < PB ? 1 : 0) : 0;
+    // full partitions from `skip` on (the skipped ones are full); the last
+    // partition is a partial item unless it is skipped too
+    const int sk = ok ? min(max(skip, 0), np) : 0;
+    const int nfull = ok ? max(np - (rem < PB ? 1 : 0) - sk, 0) : 0;
+    const bool has_partial = ok && rem < PB && sk < np;
     const int incl = wave_inclusive_sum(nfull);
     const int F = __builtin_amdgcn_readlane(incl, 63);
-    uint64_t cand = __builtin_amdgcn_ballot_w64(ok && rem < PB);  // sequences with a partial partition
+    uint64_t cand = __builtin_amdgcn_ballot_w64(has_partial);  // sequences with a partial partition item
     if (k >= F + __builtin_popcountll(cand)) return false;
     if (k < F) {
         const uint64_t past = __builtin_amdgcn_ballot_w64(incl > k);
         if (past == 0) return false;  // cannot happen for k < F; keeps every index in range regardless
         const int s = __builtin_ctzll(past);
         seq = s;
-        part = k - (__builtin_amdgcn_readlane(incl, s) - __builtin_amdgcn_readlane(nfull, s));
+        part = __builtin_amdgcn_readlane(sk, s) + k - (__builtin_amdgcn_readlane(incl, s) -
+                                                        __builtin_amdgcn_readlane(nfull, s));
         return s < a.num_seqs && part >= 0 && part < __builtin_amdgcn_readlane(np, s);
     }
     k -= F;
@@ -611,6 +621,14 @@ int launch_partition(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
+
+// Shared-prefix partition states (pa_decode_prefix.hip): whether the
+// matrix-core tile covers the shape, and the launch that writes the states of
+// every group's shared partitions plus the per-sequence skip counts.
+bool prefix_states_supported(int kv_dtype, int q_dtype, int head_dim, int block_size, int group);
+int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int32_t* group_start,
+                         const int32_t* group_prefix, int num_groups, int max_group_size, int max_prefix_len,
+                         int32_t* skip, hipStream_t stream);
 
 // Per-format dispatch over head_dim, block_size and group size; defined in
 // one translation unit per KV format.

@@ -1,0 +1,196 @@
+// Shared-prefix decode: the partitions of a prompt that several sequences
+// share (the beams of one prompt, forked with every block shared) are read
+// once for all of them.
+//
+// Sequences form groups (group_start); the first group_prefix[g] tokens of
+// every member of group g live in the same physical blocks, named by the
+// members' tables (the leader's -- the group's first sequence -- are read).
+// With partition size P, the first floor(group_prefix[g] / P) partitions are
+// whole shared partitions.  For each (group, kv head, shared partition) one
+// workgroup runs the multi-query tile of pa_mq_mfma.hpp with every member's
+// G query heads as columns (64 / G members per workgroup) over the
+// partition's P keys, and writes each member's partition state (m, l, acc)
+// into the same workspace slots the decode partition kernel uses; a member
+// with a single partition gets its output row directly.  The decode
+// partition kernel then skips those partitions (skip_parts) and the reduce
+// kernel merges all of a sequence's partitions as usual.
+//
+// A member that holds fewer tokens than the shared partitions (or whose
+// length is invalid) is not shared: its skip is 0 and the decode kernels
+// compute it alone.  A leader shorter than the shared partitions disables
+// sharing for its group.
+#include "pa_mq_mfma.hpp"
+
+namespace pa {
+
+struct PrefixArgs {
+    DecodeArgs d;
+    MqPool pool;
+    const int32_t* group_start;   // [num_groups + 1]
+    const int32_t* group_prefix;  // [num_groups] shared tokens
+    int num_groups;
+    int chunks;                   // member chunks per group in the grid
+    int parts;                    // shared partitions per group in the grid
+    int32_t* skip;                // [num_seqs] written here, read by the decode plan
+};
+
+template <Fmt KV, int D, int BS, int G>
+__global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs a) {
+    using Sh = MqShape<D, BS, G>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const DecodeArgs& d = a.d;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int H = d.num_kv_heads;
+    const int P = d.partition_size;
+
+    int rest = blockIdx.x;
+    const int kvh = rest % H;
+    rest /= H;
+    const int chunk = rest % a.chunks;
+    rest /= a.chunks;
+    const int part = rest % a.parts;
+    const int grp = rest / a.parts;
+
+    const int s0 = a.group_start[grp];
+    const int s1 = a.group_start[grp + 1];
+    auto length_ok = [&](int T) {
+        return T > 0 && T <= d.max_seq_len && (T + BS - 1) / BS <= d.max_blocks_per_seq;
+    };
+    const bool members_ok = 0 <= s0 && s0 <= s1 && s1 <= d.num_seqs;
+    int nparts = 0;  // shared partitions of the group
+    if (members_ok && s1 > s0) {
+        const int pre = a.group_prefix[grp];
+        const int T0 = d.seq_lens[s0];
+        nparts = pre > 0 ? min(pre / P, a.parts) : 0;  // never more than the grid covers
+        if (!length_ok(T0) || T0 < nparts * P) nparts = 0;  // the leader must hold the shared partitions
+    }
+    auto shares = [&](int T) { return nparts > 0 && length_ok(T) && T >= nparts * P; };
+
+    // the skips of the group's members (and of the sequences before the
+    // first group and after the last one, which no group covers)
+    if (part == 0 && chunk == 0 && kvh == 0) {
+        if (members_ok)
+            for (int i = s0 + (int)threadIdx.x; i < s1; i += 256)  // members past the grid's chunks: alone
+                a.skip[i] = (i - s0 < a.chunks * Sh::TQ && shares(d.seq_lens[i])) ? nparts : 0;
+        if (grp == 0)
+            for (int i = threadIdx.x; i < min(max(s0, 0), d.num_seqs); i += 256) a.skip[i] = 0;
+        if (grp == a.num_groups - 1)
+            for (int i = max(s1, 0) + (int)threadIdx.x; i < d.num_seqs; i += 256) a.skip[i] = 0;
+    }
+    if (!members_ok || part >= nparts) return;
+    const int members = s1 - s0;
+    const int mem_lo = chunk * Sh::TQ;
+    if (mem_lo >= members) return;
+
+    // this lane's column: member mem_lo + wave * (16 / G) + n / G, head n % G
+    const int mi = mem_lo + wave * Sh::PER_WAVE + n / G;
+    const int seq = s0 + (mi < members ? mi : 0);
+    const int head = kvh * G + n % G;
+    const int T = d.seq_lens[seq];
+    MqTask t;
+    t.bt = d.block_tables + (size_t)s0 * d.max_blocks_per_seq;
+    t.key_begin = part * P;
+    t.key_end = (part + 1) * P;
+    t.kv_len = t.key_end;
+    t.kvh = kvh;
+    t.cvalid = mi < members && shares(T);
+    t.cpos = t.key_end - 1;
+    t.qptr = (const char*)d.q + (((size_t)seq * d.num_heads + head) * D + 32 * g) * 2;
+    t.wave_cols = mem_lo + wave * Sh::PER_WAVE < members;
+    t.wpos_min = t.key_end - 1;
+    t.wpos_max = t.key_end - 1;
+
+    float m, l;
+    f32x4 acc[2][4];
+    bool bad;
+    mq_tile<KV, D, BS, G>(a.pool, t, smem, m, l, acc, bad);
+
+    if (!t.cvalid) return;
+    const size_t row = (size_t)seq * d.num_heads + head;
+    const float nan = __builtin_nanf("");
+    if ((T + P - 1) / P == 1) {  // the sequence is this one shared partition: finish its row
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    store_out(d.out, d.out_dtype, row * D + 64 * aa + 16 * g + 4 * i + b,
+                              bad ? nan : acc[aa][b][i] * inv);
+        return;
+    }
+    const size_t pidx = row * d.max_partitions + part;
+    if (g == 0) {
+        store_stream(&d.part_m[pidx], bad ? nan : m);
+        store_stream(&d.part_l[pidx], bad ? nan : l);
+    }
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                store_stream(&d.part_acc[pidx * D + 64 * aa + 16 * g + 4 * i + b], bad ? nan : acc[aa][b][i]);
+}
+
+template <Fmt KV, int D, int BS, int G>
+static int launch_prefix(PrefixArgs& a, int max_group_size, int max_prefix_len, hipStream_t stream) {
+    using Sh = MqShape<D, BS, G>;
+    auto kernel = prefix_states_kernel<KV, D, BS, G>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+    if (attr != hipSuccess) return PA_ERR_LAUNCH;
+    a.chunks = max((max_group_size + Sh::TQ - 1) / Sh::TQ, 1);
+    a.parts = max(max_prefix_len / a.d.partition_size, 1);  // at least one: the skips are written by part 0
+    const long long grid = (long long)a.num_groups * a.chunks * a.parts * a.d.num_kv_heads;
+    if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if (grid == 0) return PA_OK;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), Sh::LDS, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <Fmt KV, int BS>
+static int dispatch_prefix_group(PrefixArgs& a, int group, int mgs, int mpl, hipStream_t s) {
+    switch (group) {
+        case 1: return launch_prefix<KV, 128, BS, 1>(a, mgs, mpl, s);
+        case 2: return launch_prefix<KV, 128, BS, 2>(a, mgs, mpl, s);
+        case 4: return launch_prefix<KV, 128, BS, 4>(a, mgs, mpl, s);
+        case 8: return launch_prefix<KV, 128, BS, 8>(a, mgs, mpl, s);
+    }
+    return PA_ERR_UNSUPPORTED;
+}
+
+bool prefix_states_supported(int kv_dtype, int q_dtype, int head_dim, int block_size, int group) {
+    return ((kv_dtype == PA_DTYPE_BF16 && q_dtype == PA_DTYPE_BF16) ||
+            (kv_dtype == PA_DTYPE_F16 && q_dtype == PA_DTYPE_F16)) &&
+           head_dim == 128 && (block_size == 16 || block_size == 32) &&
+           (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int32_t* group_start,
+                         const int32_t* group_prefix, int num_groups, int max_group_size, int max_prefix_len,
+                         int32_t* skip, hipStream_t stream) {
+    PrefixArgs a;
+    a.d = d;
+    a.pool.k_cache = d.k_cache;
+    a.pool.v_cache = d.v_cache;
+    a.pool.num_kv_heads = d.num_kv_heads;
+    a.pool.num_blocks = d.num_blocks;
+    a.pool.qk_scale_log2 = d.qk_scale_log2;
+    a.group_start = group_start;
+    a.group_prefix = group_prefix;
+    a.num_groups = num_groups;
+    a.skip = skip;
+    if (kv_dtype == PA_DTYPE_BF16)
+        return d.block_size == 16 ? dispatch_prefix_group<Fmt::BF16, 16>(a, group, max_group_size, max_prefix_len, stream)
+                                  : dispatch_prefix_group<Fmt::BF16, 32>(a, group, max_group_size, max_prefix_len, stream);
+    return d.block_size == 16 ? dispatch_prefix_group<Fmt::F16, 16>(a, group, max_group_size, max_prefix_len, stream)
+                              : dispatch_prefix_group<Fmt::F16, 32>(a, group, max_group_size, max_prefix_len, stream);
+}
+
+}  // namespace pa

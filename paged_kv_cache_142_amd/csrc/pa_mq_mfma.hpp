@@ -1,0 +1,364 @@
+// Multi-query attention tile on the gfx950 matrix cores, shared by the
+// prefill kernel (pa_prefill.hip) and the shared-prefix kernel
+// (pa_decode_prefix.hip).
+//
+// A workgroup of four waves computes 64 query columns -- (token or sequence,
+// query head) pairs of one kv head, 16 per wave -- over a contiguous range of
+// keys read through one block-table row.  The keys are walked in steps of 32
+// (two blocks of 16 or one of 32): the step's K and V rows are copied once
+// into LDS (the four waves issue a quarter of the 16-byte asynchronous copies
+// each) and serve all 64 columns.  An S-stage ring keeps S - 1 steps of
+// copies in flight; one barrier per step separates "everyone finished step
+// k-1" from "step k+S-1 may overwrite its stage".
+//
+// Per wave, with v_mfma_f32_16x16x32 (bf16 or f16 operands, f32
+// accumulation) and lane = 16 g + n (g = 0..3, n = 0..15):
+//   scores   S^T[key][column] = K Q^T: A = K rows (lane supplies row n of
+//            the 16-key half, elements 32 g + 8 c .. + 7 for the c-th of four
+//            products over head_dim 128), B = the wave's query columns.  The
+//            lane receives column n's scores for keys 4 g + i, i = 0..3, of
+//            each half.
+//   softmax  per column: the lane's 8 scores, a max across the four lane
+//            groups, the running max uniform over the column's lanes; keys
+//            after the column's last visible position get -inf.
+//   values   O^T[dim][column] += V^T P^T: B = the lane's own p (split into
+//            a 16-bit high part and the rounded remainder, two products, so
+//            p keeps about 16 significant bits); A = V^T, the lane supplying
+//            dims 64 a + 4 n + b of its 8 keys (eight 8-byte LDS reads
+//            repacked by byte permutes, one product per (a, b)).  The lane
+//            receives column n's dims 64 a + 16 g + 4 i + b.
+// K rows sit in LDS XOR-swizzled by 16-byte granule (row t, granule x at
+// slot x ^ (t mod 16)) and V rows by half row (x ^ 8 when bit 2 of t is
+// set), both through the copies' source addresses, so that the reads above
+// spread over the banks.
+//
+// The physical block ids of the key range are loaded into LDS first (in
+// windows of ID_CAP blocks).  An id outside the pool is never used as an
+// address: block 0 is read instead and `bad` is set.  Rows at or beyond the
+// task's kv_len (the tail of a sequence's last block) are dropped: their
+// scores are masked and their values zeroed.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_decode_kernel.hpp"
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <Fmt F> struct MfmaOps;
+template <> struct MfmaOps<Fmt::BF16> {
+    typedef bf16x8 vec;
+    typedef __bf16 elem;
+    __device__ static __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct MfmaOps<Fmt::F16> {
+    typedef f16x8 vec;
+    typedef _Float16 elem;
+    __device__ static __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Maximum and sum over the four 16-lane groups (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float mq_max_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float mq_sum_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+#ifndef PA_MQ_STAGES
+#define PA_MQ_STAGES 4
+#endif
+
+template <int D, int BS, int G>
+struct MqShape {
+    static constexpr int S = PA_MQ_STAGES;         // LDS stages (S - 1 steps of copies in flight)
+    static constexpr int W = 4;                   // waves per workgroup
+    static constexpr int COLS = 16;               // query columns per wave
+    static constexpr int TQ = W * COLS / G;       // query tokens (or sequences) per workgroup
+    static constexpr int PER_WAVE = COLS / G;     // query tokens (or sequences) per wave
+    static constexpr int STEP = 32;               // keys per step
+    static constexpr int BPS = STEP / BS;         // blocks per step
+    static constexpr int ROWB = D * 2;            // bytes of one K or V row
+    static constexpr int HALF = STEP * ROWB;      // K (or V) rows of one step
+    static constexpr int STAGE = 2 * HALF;
+    static constexpr int COPIES = STAGE / 1024;   // 1 KiB copies per step
+    static constexpr int COPIES_PER_WAVE = COPIES / W;
+    static constexpr int ID_CAP = 2048;           // block ids held in LDS
+    static constexpr int IDS_AT = S * STAGE;
+    static constexpr int LDS = IDS_AT + ID_CAP * 4 + 16;
+    static_assert(D == 128, "the lane roles assume head_dim 128");
+    static_assert(BS == 16 || BS == 32, "block size");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
+    static_assert(COPIES % W == 0, "copies split evenly over the waves");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
+    static_assert(S >= 2 && S <= 4, "the waits below cover two to four stages");
+};
+
+// The pool and the score scale.
+struct MqPool {
+    const void* k_cache;
+    const void* v_cache;
+    int num_kv_heads;
+    int num_blocks;
+    float qk_scale_log2;  // scale * log2(e)
+};
+
+// One workgroup's tile: the key range (block aligned start), and this lane's
+// column.
+struct MqTask {
+    const int32_t* bt;   // block-table row that holds the key range
+    int key_begin;       // first key; a multiple of the block size
+    int key_end;         // one past the last key any column sees
+    int kv_len;          // rows at or beyond this key hold no data
+    int kvh;
+    const void* qptr;    // the lane's query elements 32 g .. 32 g + 31 (read only when cvalid)
+    bool cvalid;         // the lane's column exists
+    int cpos;            // last key the lane's column sees
+    bool wave_cols;      // the wave has at least one column
+    int wpos_min;        // smallest and largest last-visible key over the wave's columns
+    int wpos_max;
+};
+
+// Runs the tile.  On return every lane holds its column's running max m (log2
+// units, uniform over the column's lanes), the sum l over all its lanes, and
+// the unnormalised accumulators acc[a][b][i] for dims 64 a + 16 g + 4 i + b;
+// `bad` is set when the table named a block outside the pool.  All threads of
+// the workgroup must call it.
+template <Fmt KV, int D, int BS, int G>
+__device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& m, float& l, f32x4 (&acc)[2][4],
+                        bool& bad) {
+    using Sh = MqShape<D, BS, G>;
+    using Ops = MfmaOps<KV>;
+    using vec = typename Ops::vec;
+    constexpr int ROWB = Sh::ROWB, STEP = Sh::STEP, BPS = Sh::BPS, S = Sh::S;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int H = pool.num_kv_heads;
+    const int kvh = t.kvh;
+
+    // ---- queries of this lane's column (zero for missing columns)
+    vec qop[4];
+    {
+        const u32x4* qp = (const u32x4*)t.qptr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 v = t.cvalid ? qp[c] : u32x4{0, 0, 0, 0};
+            qop[c] = __builtin_bit_cast(vec, v);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[c]));  // resident before the copies start
+    }
+
+    // ---- block ids of the key range into LDS, in windows of ID_CAP
+    int* ids = (int*)(smem + Sh::IDS_AT);
+    int* bad_flag = ids + Sh::ID_CAP;
+    const int blk0 = t.key_begin / BS;                  // first block of the range
+    const int nblk = (t.key_end - 1) / BS + 1 - blk0;   // blocks of the range
+    auto load_ids = [&](int first) {
+        const int cnt = min(Sh::ID_CAP, nblk - first);
+        for (int j = threadIdx.x; j < cnt; j += 256) {
+            int id = t.bt[blk0 + first + j];
+            if ((unsigned)id >= (unsigned)pool.num_blocks) {
+                *bad_flag = 1;
+                id = 0;
+            }
+            ids[j] = id;
+        }
+    };
+    if (threadIdx.x == 0) *bad_flag = 0;
+    __syncthreads();
+    int window = 0;  // first block (relative to blk0) held in `ids`
+    load_ids(0);
+    __syncthreads();
+
+    // ---- copies of one step: wave w copies COPIES_PER_WAVE 1 KiB pieces;
+    // piece p < COPIES/2 is K, the rest V; each covers 4 rows of 256 bytes
+    const char* kc = (const char*)pool.k_cache;
+    const char* vc = (const char*)pool.v_cache;
+    const uint32_t lds0 = lds_addr_of(smem);
+    auto issue = [&](int k, int stage) {
+#pragma unroll
+        for (int j = 0; j < Sh::COPIES_PER_WAVE; ++j) {
+            const int piece = wave * Sh::COPIES_PER_WAVE + j;
+            const bool is_v = piece >= Sh::COPIES / 2;
+            const int pk = is_v ? piece - Sh::COPIES / 2 : piece;
+            const int row = pk * 4 + lane / 16;                 // key row inside the step
+            const int slot = lane % 16;                          // 16-byte slot in the LDS row
+            const int gran = is_v ? (slot ^ (((row >> 2) & 1) << 3)) : (slot ^ (row & 15));
+            const int blk = k * BPS + row / BS;                  // block index relative to blk0
+            const int b0 = k * BPS;                              // the step's first block
+            const int use = blk < nblk ? blk : b0;               // past the last block: reread the first
+            const int pb = ids[use - window];
+            const size_t src = (((size_t)pb * H + kvh) * BS + row % BS) * ROWB + gran * 16;
+            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE + (is_v ? Sh::HALF : 0) + pk * 1024);
+            dma16_to_lds_stream((is_v ? vc : kc) + src, dst);
+        }
+    };
+
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[aa][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float qk_scale = pool.qk_scale_log2;
+    const int cpos = t.cvalid ? t.cpos : -1;  // missing columns see no key
+
+    // LDS read offsets that do not depend on the step
+    const int kslot[4] = {(4 * g + 0) ^ n, (4 * g + 1) ^ n, (4 * g + 2) ^ n, (4 * g + 3) ^ n};
+
+    auto step = [&](const char* st, int k0, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const char* kb = st;
+        const char* vb = st + Sh::HALF;
+        // scores of both 16-key halves: sc[h][i] is key k0 + 16 h + 4 g + i
+        f32x4 sc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const char* rowp = kb + (16 * h + n) * ROWB;
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                c = Ops::mma(__builtin_bit_cast(vec, *(const u32x4*)(rowp + kslot[cc] * 16)), qop[cc], c);
+            sc[h] = c;
+        }
+        float s[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = !MASKED || k0 + 16 * h + 4 * g + i <= cpos;
+                s[h][i] = ok ? sc[h][i] * qk_scale : -INFINITY;
+            }
+        float mx = s[0][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[h][i]);
+        mx = mq_max_groups(mx);
+        const float mn = fmaxf(m, mx);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {
+            const float alpha = fast_exp2(m - mu);
+            l *= alpha;
+#pragma unroll
+            for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[aa][b] *= alpha;
+        }
+        m = mn;
+        vec phi, plo;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[h][i] - mu);
+                l += p;
+                const typename Ops::elem ph = (typename Ops::elem)p;
+                phi[4 * h + i] = ph;
+                plo[4 * h + i] = (typename Ops::elem)(p - (float)ph);
+            }
+        // values: dims 64 a + 4 n + b of keys 16 h + 4 g + i, one product per (a, b)
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+            u32x2 w[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * h + 4 * g + i;
+                    const int gran = (8 * aa + n / 2) ^ (((row >> 2) & 1) << 3);
+                    w[h][i] = *(const u32x2*)(vb + row * ROWB + gran * 16 + (n & 1) * 8);
+                    if constexpr (MASKED) {
+                        if (k0 + row >= t.kv_len) w[h][i] = u32x2{0u, 0u};  // rows past the data may hold anything
+                    }
+                }
+            // operand b, element 4 h + i = element b of w[h][i]: pairs of keys
+            // share a 32-bit word
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                u32x4 op;
+                const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int ip = 0; ip < 2; ++ip) {
+                        const uint32_t lo = w[h][2 * ip][b >> 1];
+                        const uint32_t hi = w[h][2 * ip + 1][b >> 1];
+                        op[2 * h + ip] = __builtin_amdgcn_perm(hi, lo, sel);
+                    }
+                const vec A = __builtin_bit_cast(vec, op);
+                acc[aa][b] = Ops::mma(A, phi, acc[aa][b]);
+                acc[aa][b] = Ops::mma(A, plo, acc[aa][b]);
+            }
+        }
+    };
+
+    // ---- main loop over 32-key steps, S - 1 steps of copies ahead.  The
+    // first S - 1 steps never need a new id window (S - 1 < ID_CAP / BPS).
+    const int nsteps = (t.key_end - t.key_begin + STEP - 1) / STEP;
+    const int steps_per_window = Sh::ID_CAP / BPS;
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        if (k < nsteps) issue(k, k);
+    for (int k = 0; k < nsteps; ++k) {
+        // this wave's copies of step k are complete when at most those of the
+        // later steps already issued (up to S - 2 of them) are in flight
+        const int later = min(S - 2, nsteps - 1 - k);
+        if constexpr (S >= 4) {
+            if (later >= 2) wait_vmcnt<2 * Sh::COPIES_PER_WAVE>();
+            else if (later == 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
+            else wait_vmcnt<0>();
+        } else if constexpr (S == 3) {
+            if (later >= 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();  // everyone's copies of step k landed; step k-1 is finished everywhere
+        const int kn = k + S - 1;  // the step whose copies go out now, into step k-1's stage
+        if (kn < nsteps) {
+            if (kn % steps_per_window == 0) {  // its ids are in the next window
+                window = kn * BPS;
+                load_ids(window);
+                __syncthreads();
+            }
+            issue(kn, kn % S);
+        }
+        const int k0 = t.key_begin + k * STEP;
+        if (t.wave_cols && k0 <= t.wpos_max) {  // some column of this wave sees keys of this step
+            const char* st = smem + (k % S) * Sh::STAGE;
+            if (k0 + STEP - 1 <= t.wpos_min && k0 + STEP <= t.kv_len)
+                step(st, k0, std::false_type{});
+            else
+                step(st, k0, std::true_type{});
+        }
+    }
+    l = mq_sum_groups(l);
+    bad = *bad_flag != 0;
+}
+
+}  // namespace pa

@@ -43,13 +43,17 @@ def test_status_strings(lib):
 
 def test_workspace_size_formula(lib):
     # m, l, acc[N][H][P][D] float32 arrays, each padded to 256 bytes, then the
-    # work plan: 64 header ints and one int per (sequence, partition)
+    # work plan: 64 header ints and one int per (sequence, partition), padded
+    # too; then one int per sequence (partitions a shared prefix covers)
     n, h, d, msl, p = 64, 32, 128, 4096, 512
     parts = 8
     rows = n * h * parts
     pad = lambda x: (x + 255) // 256 * 256
-    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == 2 * pad(rows * 4) + pad(rows * d * 4) + 4 * (64 + n * parts)
-    assert lib.pa_decode_workspace_size(1, 1, 64, 0, 16) == 4 * 64
+    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == (2 * pad(rows * 4) + pad(rows * d * 4)
+                                                             + pad(4 * (64 + n * parts)) + 4 * n)
+    assert lib.pa_decode_workspace_size(3, 2, 64, 100, 16) == (2 * pad(3 * 2 * 7 * 4) + pad(3 * 2 * 7 * 64 * 4)
+                                                              + pad(4 * (64 + 3 * 7)) + 4 * 3)
+    assert lib.pa_decode_workspace_size(1, 1, 64, 0, 16) == 256 + 4
     assert lib.pa_decode_workspace_size(-1, 1, 64, 10, 16) == 0
     assert lib.pa_decode_workspace_size(1, 1, 64, 10, 0) == 0
 
@@ -170,6 +174,36 @@ def test_decode_validation(lib, fn):
     assert _dec(lib, fn, q=FAKE + 4) == SHAPE             # misaligned
     need = lib.pa_decode_workspace_size(64, 32, 128, 4096, 512)
     assert _dec(lib, fn, ws_bytes=need - 1) == WS
+
+
+def _sp(lib, gs=FAKE, gp=FAKE, groups=4, mgs=16, mpl=1024, **kw):
+    a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, k_cache=FAKE, v_cache=FAKE, kv_dtype=BF16,
+             tables=FAKE, max_blocks=256, seq_lens=FAKE, max_seq_len=4096, num_seqs=64, heads=32, kv_heads=8,
+             dim=128, block=16, blocks=9000, scale=0.088, k_scale=None, v_scale=None, part=512, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.pa_decode_shared_prefix(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k_cache"], a["v_cache"],
+                                       a["kv_dtype"], a["tables"], a["max_blocks"], a["seq_lens"], a["max_seq_len"],
+                                       a["num_seqs"], a["heads"], a["kv_heads"], a["dim"], a["block"], a["blocks"],
+                                       ctypes.c_float(a["scale"]), a["k_scale"], a["v_scale"], a["part"], a["ws"],
+                                       a["ws_bytes"], None, gs, gp, groups, mgs, mpl)
+
+
+def test_shared_prefix_decode_validation(lib):
+    # every check of pa_decode comes first, then the grouping arguments; all of
+    # these return before any launch
+    assert _sp(lib, num_seqs=0) == OK
+    assert _sp(lib, q_dtype=F16) == DTYPE
+    assert _sp(lib, heads=30) == SHAPE
+    assert _sp(lib, part=500) == SHAPE
+    assert _sp(lib, tables=None) == NULL
+    need = lib.pa_decode_workspace_size(64, 32, 128, 4096, 512)
+    assert _sp(lib, ws_bytes=need - 1) == WS
+    assert _sp(lib, groups=-1) == SHAPE
+    assert _sp(lib, mgs=-1) == SHAPE
+    assert _sp(lib, mpl=-1) == SHAPE
+    assert _sp(lib, gs=None) == NULL
+    assert _sp(lib, gp=None) == NULL
 
 
 def _pf(lib, **kw):

@@ -17,6 +17,7 @@ import torch
 import oracle
 import paged_kv_cache_142_amd as pa
 import workloads
+from workloads.generators import round_to_storage
 from gpu_util import TOL, assert_close, out_as_f64, poison_device, poison_host, to_device, to_host_raw
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +109,197 @@ def test_shared_prefix_beams(prompt_len, seed):
     got = out_as_f64(out)
     assert_close(got, logical, TOL["bf16"], f"shared_prefix p={prompt_len}")
     assert_close(got[wl.extreme], logical[wl.extreme], TOL["bf16"], "extreme-logit half")
+
+
+def _beam_groups(wl):
+    """Groups of the beams of each prompt and the tokens their tables share:
+    the prompt's whole blocks (a partially filled boundary block may have been
+    copied on write)."""
+    starts = torch.arange(0, wl.num_seqs + 1, wl.beams, dtype=torch.int32, device="cuda")
+    shared = (wl.prompt_len // wl.block_size) * wl.block_size
+    prefix = torch.full((wl.num_prompts,), shared, dtype=torch.int32, device="cuda")
+    return starts, prefix, shared
+
+
+@pytest.mark.parametrize("prompt_len,partition_size", [(1032, 512), (1024, 512), (1032, 256), (1024, 1024)])
+def test_shared_prefix_decode_beams(prompt_len, partition_size):
+    """pa_decode_shared_prefix over the forked beams: the oracle's plain
+    attention over each beam's logical rows, and pa_decode's output."""
+    seed = 3
+    wl = workloads.shared_prefix(seed, prompt_len=prompt_len)
+    print(f"[case] shared_prefix_decode prompt={prompt_len} P={partition_size}", flush=True)
+    bm, beams, kc, vc, hk, hv, tables, pairs = _assemble(wl, seed)
+    lens = wl.seq_lens()
+    msl = int(lens.max())
+    starts, prefix, shared = _beam_groups(wl)
+    q = to_device(wl.q, "bf16")
+    t_dev, l_dev = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    ws = torch.empty(pa.pa_decode_workspace_size(wl.num_seqs, wl.num_heads, wl.head_dim, msl, partition_size),
+                     dtype=torch.uint8, device="cuda")
+    out = poison_device((wl.num_seqs, wl.num_heads, wl.head_dim), "f32")
+    pa.pa_decode_shared_prefix(out, q, kc, vc, t_dev, l_dev, msl, float(wl.scale), partition_size, ws,
+                               group_start=starts, group_prefix=prefix, max_group_size=wl.beams,
+                               max_prefix_len=shared)
+    plain = poison_device((wl.num_seqs, wl.num_heads, wl.head_dim), "f32")
+    pa.pa_decode(plain, q, kc, vc, t_dev, l_dev, msl, float(wl.scale), partition_size, ws)
+    torch.cuda.synchronize()
+    expect = oracle.paged_decode(wl.q, "bf16", hk, hv, "bf16", tables, lens, wl.block_size, float(wl.scale))
+    got = out_as_f64(out)
+    assert_close(got, expect, TOL["bf16"], "shared-prefix decode")
+    assert_close(got[wl.extreme], expect[wl.extreme], TOL["bf16"], "extreme-logit half")
+    assert_close(got, out_as_f64(plain), TOL["bf16"], "shared-prefix decode vs pa_decode")
+
+
+def _grouped_case(seed, *, num_heads, num_kv_heads, head_dim, block_size, fmt, groups):
+    """Sequences in groups whose members' tables name the same first blocks.
+
+    ``groups``: list of ``(prefix_tokens, member_lengths)``.  Every member's
+    first ``ceil(min(prefix, T) / B)`` table entries are the group's shared
+    block ids, the rest private ones; block ids are scattered over the pool
+    by a seeded permutation.  Pool contents and queries are seeded standard
+    normal draws rounded to ``fmt``.
+    """
+    rng = np.random.default_rng(seed)
+    B = block_size
+    lens, rows, starts, prefixes = [], [], [0], []
+    next_id = 0
+    for pre, members in groups:
+        nshared = -(-pre // B)
+        shared_ids = list(range(next_id, next_id + nshared))
+        next_id += nshared
+        for T in members:
+            nb = -(-T // B)
+            own = min(nb, nshared)
+            row = shared_ids[:own] + list(range(next_id, next_id + nb - own))
+            next_id += nb - own
+            rows.append(row)
+            lens.append(T)
+        starts.append(len(lens))
+        prefixes.append(pre)
+    num_blocks = next_id + 5
+    perm = rng.permutation(num_blocks)
+    max_blocks = max(len(r) for r in rows) if rows else 1
+    tables = np.full((len(rows), max_blocks), -1, np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = perm[np.array(r, np.int64)]
+    shape = (num_blocks, num_kv_heads, B, head_dim)
+    hk = round_to_storage(rng.standard_normal(shape, dtype=np.float32), fmt)
+    hv = round_to_storage(rng.standard_normal(shape, dtype=np.float32), fmt)
+    q = round_to_storage(rng.standard_normal((len(lens), num_heads, head_dim), dtype=np.float32), fmt)
+    return (np.array(lens, np.int32), tables, np.array(starts, np.int32), np.array(prefixes, np.int32), hk, hv, q)
+
+
+def _run_grouped(case, *, fmt, block_size, partition_size, max_group_size=None, max_prefix_len=None,
+                 out_fmt="f32", check_plain=True, ws=None):
+    lens, tables, starts, prefixes, hk, hv, q = case
+    N, H, d = q.shape
+    msl = int(lens.max())
+    scale = 1.0 / np.sqrt(d)
+    sizes = np.diff(starts)
+    mgs = int(sizes.max()) if max_group_size is None else max_group_size
+    mpl = int(prefixes.max()) if max_prefix_len is None else max_prefix_len
+    kc, vc, qd = to_device(hk, fmt), to_device(hv, fmt), to_device(q, fmt)
+    t_dev, l_dev = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    if ws is None:
+        ws = torch.empty(pa.pa_decode_workspace_size(N, H, d, msl, partition_size), dtype=torch.uint8,
+                         device="cuda")
+    out = poison_device((N, H, d), out_fmt)
+    pa.pa_decode_shared_prefix(out, qd, kc, vc, t_dev, l_dev, msl, scale, partition_size, ws,
+                               group_start=torch.from_numpy(starts).cuda(),
+                               group_prefix=torch.from_numpy(prefixes).cuda(), max_group_size=mgs,
+                               max_prefix_len=mpl)
+    plain = poison_device((N, H, d), out_fmt)
+    if check_plain:
+        pa.pa_decode(plain, qd, kc, vc, t_dev, l_dev, msl, scale, partition_size, ws)
+    torch.cuda.synchronize()
+    expect = oracle.paged_decode(q, fmt, hk, hv, fmt, tables, lens, block_size, scale)
+    tol = max(TOL[fmt], TOL[out_fmt])
+    got = out_as_f64(out)
+    assert_close(got, expect, tol, "shared-prefix decode vs oracle")
+    if check_plain:
+        assert_close(got, out_as_f64(plain), tol, "shared-prefix decode vs pa_decode")
+
+
+def _mixed_groups(rng, P, n_target):
+    """Groups that exercise every sharing rule: no prefix, prefixes shorter
+    than one partition, not a multiple of it, members shorter than the
+    shared partitions, a member of exactly one partition, a short leader,
+    a single-member group, an empty group, and groups wider than one tile."""
+    g = []
+    g.append((3 * P, [3 * P + int(x) for x in rng.integers(1, 400, 5)]))           # 3 whole partitions
+    g.append((2 * P + 37, [2 * P + 37 + int(x) for x in rng.integers(0, 300, 4)]))  # 2 whole + tail
+    g.append((P - 1, [P - 1 + int(x) for x in rng.integers(1, 200, 3)]))            # below one partition
+    g.append((0, [int(x) for x in rng.integers(1, 3 * P, 2)]))                      # nothing shared
+    g.append((2 * P, [2 * P + 10, P + 3, 2 * P, 40, 2 * P + 700]))                  # short members
+    g.append((P, [P, P + 1, P]))                                                    # single-partition members
+    g.append((2 * P, [P + 5, 2 * P + 9, 2 * P + 100]))                              # short leader: none shared
+    g.append((2 * P, [2 * P + 3]))                                                  # one member
+    g.append((P, []))                                                               # empty group
+    n = sum(len(m) for _, m in g)
+    wide = max(n_target - n, 20)
+    g.append((P + P // 2, [P + P // 2 + int(x) for x in rng.integers(0, 2 * P, wide)]))  # wider than a tile
+    return g
+
+
+@pytest.mark.parametrize("heads,kv_heads,fmt,block,P,n", [
+    (32, 8, "bf16", 16, 512, 80),   # G = 4, plan-kernel work order (more than 64 sequences)
+    (32, 8, "bf16", 16, 512, 60),   # G = 4, in-kernel work order
+    (32, 4, "f16", 32, 256, 60),    # G = 8
+    (16, 16, "bf16", 16, 256, 70),  # G = 1
+    (16, 8, "bf16", 32, 512, 50),   # G = 2
+])
+def test_shared_prefix_decode_groups(heads, kv_heads, fmt, block, P, n):
+    seed = heads * 7 + kv_heads + block + P + n
+    rng = np.random.default_rng(seed)
+    groups = _mixed_groups(rng, P, n)
+    print(f"[case] shared_prefix_groups H={heads}/{kv_heads} {fmt} B={block} P={P} "
+          f"seqs={sum(len(m) for _, m in groups)}", flush=True)
+    case = _grouped_case(seed, num_heads=heads, num_kv_heads=kv_heads, head_dim=128, block_size=block, fmt=fmt,
+                         groups=groups)
+    _run_grouped(case, fmt=fmt, block_size=block, partition_size=P)
+
+
+def test_shared_prefix_decode_grid_bounds():
+    """max_group_size / max_prefix_len below the real ones: the members and
+    partitions past them are computed alone, with the same result."""
+    P = 512
+    rng = np.random.default_rng(11)
+    groups = [(3 * P, [3 * P + int(x) for x in rng.integers(0, 300, 40)]),
+              (2 * P, [2 * P + int(x) for x in rng.integers(0, 300, 7)])]
+    case = _grouped_case(11, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, fmt="bf16", groups=groups)
+    print("[case] shared_prefix grid bounds", flush=True)
+    _run_grouped(case, fmt="bf16", block_size=16, partition_size=P, max_group_size=20, max_prefix_len=P + 100)
+    _run_grouped(case, fmt="bf16", block_size=16, partition_size=P, max_group_size=0, check_plain=False)
+    _run_grouped(case, fmt="bf16", block_size=16, partition_size=P, max_prefix_len=P - 1, check_plain=False)
+
+
+def test_shared_prefix_decode_bf16_out_and_fallback_shapes():
+    """bf16 output rows; head_dim 64 (no matrix-core tile) runs pa_decode."""
+    P = 256
+    rng = np.random.default_rng(5)
+    groups = [(2 * P, [2 * P + int(x) for x in rng.integers(0, 300, 9)]), (P, [P, P + 70, 3 * P])]
+    print("[case] shared_prefix bf16 out / d=64", flush=True)
+    case = _grouped_case(5, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, fmt="bf16", groups=groups)
+    _run_grouped(case, fmt="bf16", block_size=16, partition_size=P, out_fmt="bf16")
+    case = _grouped_case(6, num_heads=32, num_kv_heads=8, head_dim=64, block_size=16, fmt="bf16", groups=groups)
+    _run_grouped(case, fmt="bf16", block_size=16, partition_size=P)
+
+
+def test_shared_prefix_decode_regrouped_workspace():
+    """Two calls on one workspace with different groupings: the second call's
+    skips replace the first's everywhere."""
+    P = 512
+    rng = np.random.default_rng(9)
+    lens_a = [3 * P + int(x) for x in rng.integers(0, 200, 12)]
+    case1 = _grouped_case(9, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16, fmt="bf16",
+                          groups=[(3 * P, lens_a)])
+    lens, tables, starts, prefixes, hk, hv, q = case1
+    print("[case] shared_prefix regrouped", flush=True)
+    ws = torch.empty(pa.pa_decode_workspace_size(len(lens), 32, 128, int(lens.max()), P), dtype=torch.uint8,
+                     device="cuda")
+    _run_grouped(case1, fmt="bf16", block_size=16, partition_size=P, check_plain=False, ws=ws)
+    # same pool and tables, now as singletons (nothing shared): stale skips must not survive
+    N = len(lens)
+    case2 = (lens, tables, np.arange(N + 1, dtype=np.int32), np.zeros(N, np.int32), hk, hv, q)
+    _run_grouped(case2, fmt="bf16", block_size=16, partition_size=P, max_prefix_len=3 * P, check_plain=False,
+                 ws=ws)

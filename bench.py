@@ -47,7 +47,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="gqa",
                    choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow",
-                            "prefill", "prefill_chunk"])
+                            "shared_prefix_grouped", "shared_prefix_cow_grouped", "prefill", "prefill_chunk"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -261,10 +261,10 @@ def run_prefill(args):
 
 def _workload(name, seed, partition_size):
     import workloads
-    if name == "shared_prefix":
-        return shared_prefix_step(seed, partition_size, 1024)
-    if name == "shared_prefix_cow":
+    if name.startswith("shared_prefix_cow"):
         return shared_prefix_step(seed, partition_size, 1032)
+    if name.startswith("shared_prefix"):
+        return shared_prefix_step(seed, partition_size, 1024)
     if name == "gqa":
         return workloads.gqa(seed, partition_size=partition_size)
     if name == "mha":
@@ -298,7 +298,7 @@ class Device:
     K/V in the 256 MB Infinity Cache (MALL) once the copies together exceed it.
     """
 
-    def __init__(self, wl, pools=1):
+    def __init__(self, wl, pools=1, groups=None):
         import torch
         import paged_kv_cache_142_amd as pa
         self.pa, self.torch, self.wl = pa, torch, wl
@@ -348,14 +348,27 @@ class Device:
                           scale=float(wl.scale), partition_size=wl.partition_size, workspace=self.ws,
                           k_scale=self.k_scale, v_scale=self.v_scale, kv_dtype=kv)
         self.dargs = dargs
+        # beam groups: decode through pa_decode_shared_prefix, which reads the
+        # shared prompt partitions once per group
+        self.groups = None
+        if groups is not None:
+            starts, prefix = groups
+            self.groups = dict(group_start=torch.from_numpy(starts).to(dev),
+                               group_prefix=torch.from_numpy(prefix).to(dev),
+                               max_group_size=int(np.diff(starts).max()), max_prefix_len=int(prefix.max()))
         self.pools = [(self.k_cache, self.v_cache)] + [(self.k_cache.clone(), self.v_cache.clone())
                                                         for _ in range(pools - 1)]
         # identical calls every step: marshal the C arguments once per pool copy
         self.call_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
-        self.decode_calls = [pa.prepared("pa_decode", **dict(self.dargs, k_cache=kc, v_cache=vc))
-                             for kc, vc in self.pools]
+        self.decode_calls = [self._decode_call(kc, vc) for kc, vc in self.pools]
         self.calls = self.call_sets[0]
         torch.cuda.synchronize()
+
+    def _decode_call(self, kc, vc):
+        dargs = dict(self.dargs, k_cache=kc, v_cache=vc)
+        if self.groups is not None:
+            return self.pa.prepared("pa_decode_shared_prefix", **dargs, **self.groups)
+        return self.pa.prepared("pa_decode", **dargs)
 
     def _make_calls(self, k_cache=None, v_cache=None):
         pa, kv = self.pa, self.kv
@@ -367,9 +380,12 @@ class Device:
                    if self.quantize_step else
                    pa.prepared("pa_reshape_and_cache", self.step_keys, self.step_values, kc, vc,
                                self.step_slots, kv_dtype=kv))
+        copy = pa.prepared("pa_copy_blocks", kc, vc, self.pairs, kv_dtype=kv) if self.pairs.numel() else (lambda: None)
+        if self.groups is not None:  # one call: prefix states, partitions, reduce
+            return [scatter, copy, self._decode_call(kc, vc), lambda: None]
         return [
             scatter,
-            pa.prepared("pa_copy_blocks", kc, vc, self.pairs, kv_dtype=kv) if self.pairs.numel() else (lambda: None),
+            copy,
             pa.prepared("pa_decode_partition", **dargs),
             pa.prepared("pa_decode_reduce", **dargs),
         ]
@@ -485,7 +501,14 @@ def main():
     if args.graph and args.pools != 1:
         print("--graph replays one captured step and cannot rotate pool copies; use --pools 1", file=sys.stderr)
         sys.exit(2)
-    dev = Device(wl, pools=args.pools)
+    groups = None
+    if args.config.endswith("_grouped"):  # 8 prompts x 6 beams, consecutive; the prompt's whole blocks are shared
+        beams = 6
+        starts = np.arange(0, wl.num_seqs + 1, beams, dtype=np.int32)
+        prompt_len = 1032 if args.config.startswith("shared_prefix_cow") else 1024
+        shared = prompt_len // wl.block_size * wl.block_size
+        groups = (starts, np.full(len(starts) - 1, shared, np.int32))
+    dev = Device(wl, pools=args.pools, groups=groups)
     graph = None
     if args.graph:  # one eager step first (one-time kernel attribute setup), then capture
         dev.step()
@@ -534,14 +557,27 @@ def main():
     def pct(a, b, q):
         return float(np.percentile([e[a].elapsed_time(e[b]) for e in evs], q)) * 1e3
 
-    k_us = {"reshape_and_cache": avg(0, 1), "copy_blocks": avg(1, 2), "decode_partition": avg(2, 3),
-            "decode_reduce": avg(3, 4)}
-    k_us["decode"] = k_us["decode_partition"] + k_us["decode_reduce"]
+    if groups is not None:
+        k_us = {"reshape_and_cache": avg(0, 1), "copy_blocks": avg(1, 2), "decode": avg(2, 3)}
+    else:
+        k_us = {"reshape_and_cache": avg(0, 1), "copy_blocks": avg(1, 2), "decode_partition": avg(2, 3),
+                "decode_reduce": avg(3, 4)}
+        k_us["decode"] = k_us["decode_partition"] + k_us["decode_reduce"]
     kv_bytes = wl.kv_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    part_bytes = partition_algorithmic_bytes(wl)
-    achieved = part_bytes / (k_us["decode_partition"] * 1e-6) / 1e9
-    traffic = _traffic(wl)
+    if groups is not None:
+        # the three launches together against the distinct bytes they must read
+        part_bytes = unique_kv_bytes(wl)
+        achieved = part_bytes / (k_us["decode"] * 1e-6) / 1e9
+        roof_kernel = ("pa_decode_shared_prefix (prefix states, partition and reduce launches together) over the "
+                       "distinct K/V bytes")
+        traffic = None
+    else:
+        part_bytes = partition_algorithmic_bytes(wl)
+        achieved = part_bytes / (k_us["decode_partition"] * 1e-6) / 1e9
+        roof_kernel = ("pa_decode_partition launch (the partition kernel; preceded by decode_plan_kernel "
+                       "above 64 sequences)")
+        traffic = _traffic(wl)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -558,12 +594,12 @@ def main():
         "decode_alone_GBs": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9, 2),
         "decode_alone_hbm_frac": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
-        "decode_partition_us_p10_p90": [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
+        "decode_partition_us_p10_p90" if groups is None else "decode_us_p10_p90":
+            [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
         "pool_copies": args.pools,
-        "roofline": {"kernel": "pa_decode_partition launch (the partition kernel; preceded by decode_plan_kernel "
-                               "above 64 sequences)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": roof_kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }
@@ -572,6 +608,9 @@ def main():
         line["config"]["cache_assisted"] = ("prompt blocks are shared by 6 beams: the logical KV bytes are read "
                                             "from far fewer distinct bytes, which fit in the Infinity Cache")
         line["unique_kv_GBs"] = round(unique_kv_bytes(wl) / (ms_per_step * 1e-3) / 1e9, 2)
+        if groups is not None:
+            line["config"]["decode"] = ("pa_decode_shared_prefix: groups of 6 beams, the prompt's whole blocks "
+                                        f"({int(groups[1][0])} tokens) shared")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -296,7 +296,8 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
  * A member holding fewer tokens than its group's shared partitions is
  * computed alone; so is a whole group whose first sequence is that short.
  * Shapes the matrix-core path does not cover (FP8 or F32 KV, head_dim 64,
- * G = 16) and num_groups == 0 run pa_decode unchanged.
+ * G = 16), an `out` that is not 16-byte aligned and num_groups == 0 run
+ * pa_decode unchanged.
  */
 int pa_decode_shared_prefix(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
                             const void* v_cache, int kv_dtype, const int32_t* block_tables,
@@ -323,14 +324,16 @@ int pa_decode_shared_prefix(void* out, int out_dtype, const void* q, int q_dtype
  * (0h-n0.github.io explainer, section "Attention計算", restricted to the keys
  * up to p).  Q == T is a full prefill, Q < T a chunk appended to a context.
  *
- * Method: one workgroup per (sequence, tile of 64/G query tokens, kv head);
- * the tile's 64 (token, head) columns share each staged 32-key K/V step, and
+ * Method: one workgroup per (tile of 128/G query tokens of one sequence, kv
+ * head); the tile's 128 (token, head) columns share each staged 32-key K/V
+ * step, and
  * the score and value products run on the matrix cores (v_mfma_f32_16x16x32,
  * fp32 accumulation; softmax weights enter the value product as a 16-bit
  * high part plus remainder) with the online-softmax recurrence of equation
  * (4) of the same review per column.
  *
- *   out          [total_q][num_heads][head_dim], out_dtype (F32, F16 or BF16)
+ *   out          [total_q][num_heads][head_dim], out_dtype (F32, F16 or BF16),
+ *                16-byte aligned
  *   q            [total_q][num_heads][head_dim], q_dtype, 16-byte aligned
  *   query_start  [num_seqs + 1] int32, device; non-decreasing, last = total_q
  *   max_query_len  host upper bound of the per-sequence query counts (sizes

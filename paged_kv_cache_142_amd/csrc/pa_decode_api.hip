@@ -384,7 +384,7 @@ extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_st
     if (num_groups > 0 && (!group_start || !group_prefix)) return PA_ERR_NULL;
     const hipStream_t s = (hipStream_t)stream;
     // nothing to share, or a shape the matrix-core tile does not cover: plain decode
-    if (num_groups == 0 || max_prefix_len < partition_size || max_group_size == 0 ||
+    if (num_groups == 0 || max_prefix_len < partition_size || max_group_size == 0 || ((uintptr_t)out & 15u) ||
         !pa::prefix_states_supported(pr.kv_dtype, pr.q_dtype, pr.head_dim, block_size, pr.group)) {
         const int s1 = pa::run_partition(pr, s);
         if (s1 != PA_OK) return s1;

@@ -21,6 +21,10 @@
 // sharing for its group.
 #include "pa_mq_mfma.hpp"
 
+#ifndef PA_PREFIX_STAGES
+#define PA_PREFIX_STAGES 4
+#endif
+
 namespace pa {
 
 struct PrefixArgs {
@@ -36,7 +40,7 @@ struct PrefixArgs {
 
 template <Fmt KV, int D, int BS, int G>
 __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs a) {
-    using Sh = MqShape<D, BS, G>;
+    using Sh = MqShape<D, BS, G, 1, PA_PREFIX_STAGES>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const DecodeArgs& d = a.d;
 
@@ -91,37 +95,38 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
     const int seq = s0 + (mi < members ? mi : 0);
     const int head = kvh * G + n % G;
     const int T = d.seq_lens[seq];
-    MqTask t;
+    MqTask<1> t;
     t.bt = d.block_tables + (size_t)s0 * d.max_blocks_per_seq;
     t.key_begin = part * P;
     t.key_end = (part + 1) * P;
     t.kv_len = t.key_end;
     t.kvh = kvh;
-    t.cvalid = mi < members && shares(T);
-    t.cpos = t.key_end - 1;
-    t.qptr = (const char*)d.q + (((size_t)seq * d.num_heads + head) * D + 32 * g) * 2;
+    t.cvalid[0] = mi < members && shares(T);
+    t.cpos[0] = t.key_end - 1;
+    t.qptr[0] = (const char*)d.q + (((size_t)seq * d.num_heads + head) * D + 32 * g) * 2;
     t.wave_cols = mem_lo + wave * Sh::PER_WAVE < members;
     t.wpos_min = t.key_end - 1;
     t.wpos_max = t.key_end - 1;
 
-    float m, l;
-    f32x4 acc[2][4];
+    float m1[1], l1[1];
+    f32x4 acc1[1][2][4];
     bool bad;
-    mq_tile<KV, D, BS, G>(a.pool, t, smem, m, l, acc, bad);
+    mq_tile<KV, D, BS, G, 1, PA_PREFIX_STAGES, true>(a.pool, t, smem, m1, l1, acc1, bad);
+    const float m = m1[0], l = l1[0];
+    const f32x4(&acc)[2][4] = acc1[0];
 
-    if (!t.cvalid) return;
+    if (!t.cvalid[0]) return;
     const size_t row = (size_t)seq * d.num_heads + head;
     const float nan = __builtin_nanf("");
+    // four consecutive dims (b = 0..3) per store
     if ((T + P - 1) / P == 1) {  // the sequence is this one shared partition: finish its row
-        const float inv = 1.f / l;
+        const float inv = bad ? nan : 1.f / l;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    store_out(d.out, d.out_dtype, row * D + 64 * aa + 16 * g + 4 * i + b,
-                              bad ? nan : acc[aa][b][i] * inv);
+                store_out4(d.out, d.out_dtype, row * D + 64 * aa + 16 * g + 4 * i,
+                           f32x4{acc[aa][0][i], acc[aa][1][i], acc[aa][2][i], acc[aa][3][i]} * inv);
         return;
     }
     const size_t pidx = row * d.max_partitions + part;
@@ -129,18 +134,18 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
         store_stream(&d.part_m[pidx], bad ? nan : m);
         store_stream(&d.part_l[pidx], bad ? nan : l);
     }
+    const float one = bad ? nan : 1.f;
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                store_stream(&d.part_acc[pidx * D + 64 * aa + 16 * g + 4 * i + b], bad ? nan : acc[aa][b][i]);
+            __builtin_nontemporal_store(f32x4{acc[aa][0][i], acc[aa][1][i], acc[aa][2][i], acc[aa][3][i]} * one,
+                                        (f32x4*)&d.part_acc[pidx * D + 64 * aa + 16 * g + 4 * i]);
 }
 
 template <Fmt KV, int D, int BS, int G>
 static int launch_prefix(PrefixArgs& a, int max_group_size, int max_prefix_len, hipStream_t stream) {
-    using Sh = MqShape<D, BS, G>;
+    using Sh = MqShape<D, BS, G, 1, PA_PREFIX_STAGES>;
     auto kernel = prefix_states_kernel<KV, D, BS, G>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);

@@ -2,12 +2,13 @@
 // prefill kernel (pa_prefill.hip) and the shared-prefix kernel
 // (pa_decode_prefix.hip).
 //
-// A workgroup of four waves computes 64 query columns -- (token or sequence,
-// query head) pairs of one kv head, 16 per wave -- over a contiguous range of
-// keys read through one block-table row.  The keys are walked in steps of 32
-// (two blocks of 16 or one of 32): the step's K and V rows are copied once
-// into LDS (the four waves issue a quarter of the 16-byte asynchronous copies
-// each) and serve all 64 columns.  An S-stage ring keeps S - 1 steps of
+// A workgroup of four waves computes 64 CB query columns -- (token or
+// sequence, query head) pairs of one kv head, CB blocks of 16 per wave --
+// over a contiguous range of keys read through one block-table row.  The keys
+// are walked in steps of 32 (two blocks of 16 or one of 32): the step's K and
+// V rows are copied once into LDS (the four waves issue a quarter of the
+// 16-byte asynchronous copies each) and serve all the columns; inside a wave
+// each K and V operand read from LDS serves its CB column blocks.  An S-stage ring keeps S - 1 steps of
 // copies in flight; one barrier per step separates "everyone finished step
 // k-1" from "step k+S-1 may overwrite its stage".
 //
@@ -88,11 +89,13 @@ __device__ __forceinline__ float mq_sum_groups(float x) {
 #define PA_MQ_STAGES 4
 #endif
 
-template <int D, int BS, int G>
+// D: head_dim; BS: block size; G: query heads per kv head; CB: 16-column
+// blocks per wave; STAGES: LDS ring depth.
+template <int D, int BS, int G, int CB = 1, int STAGES = PA_MQ_STAGES>
 struct MqShape {
-    static constexpr int S = PA_MQ_STAGES;         // LDS stages (S - 1 steps of copies in flight)
+    static constexpr int S = STAGES;              // LDS stages (S - 1 steps of copies in flight)
     static constexpr int W = 4;                   // waves per workgroup
-    static constexpr int COLS = 16;               // query columns per wave
+    static constexpr int COLS = 16 * CB;          // query columns per wave
     static constexpr int TQ = W * COLS / G;       // query tokens (or sequences) per workgroup
     static constexpr int PER_WAVE = COLS / G;     // query tokens (or sequences) per wave
     static constexpr int STEP = 32;               // keys per step
@@ -108,11 +111,40 @@ struct MqShape {
     static_assert(D == 128, "the lane roles assume head_dim 128");
     static_assert(BS == 16 || BS == 32, "block size");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
-    static_assert(COPIES % W == 0, "copies split evenly over the waves");
+    static_assert(CB == 1 || CB == 2, "column blocks per wave");
+    static_assert(COPIES % W == 0 && COPIES / 2 % COPIES_PER_WAVE == 0, "a wave copies only K or only V");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
-    static_assert(S >= 2 && S <= 4, "the waits below cover two to four stages");
+    static_assert(S >= 2 && (S - 2) * COPIES_PER_WAVE <= 63, "vmcnt holds the copies of S - 2 steps");
 };
+
+// Waits until at most `later` (< N + 1) steps of C copies each, issued after
+// the one needed now, are still in flight.
+template <int C, int N>
+__device__ __forceinline__ void wait_later_steps(int later) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (later >= N)
+            wait_vmcnt<N * C>();
+        else
+            wait_later_steps<C, N - 1>(later);
+    }
+}
+
+// Four consecutive output elements (idx a multiple of 4).
+__device__ __forceinline__ void store_out4(void* out, int dtype, size_t idx, f32x4 v) {
+    if (dtype == PA_DTYPE_F32) {
+        *(f32x4*)((float*)out + idx) = v;
+    } else if (dtype == PA_DTYPE_BF16) {
+        const uint32_t lo = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        *(u32x2*)((uint16_t*)out + idx) = u32x2{lo, hi};
+    } else {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        *(h4*)((_Float16*)out + idx) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    }
+}
 
 // The pool and the score scale.
 struct MqPool {
@@ -124,33 +156,35 @@ struct MqPool {
 };
 
 // One workgroup's tile: the key range (block aligned start), and this lane's
-// column.
+// column in each of the wave's CB column blocks.
+template <int CB>
 struct MqTask {
-    const int32_t* bt;   // block-table row that holds the key range
-    int key_begin;       // first key; a multiple of the block size
-    int key_end;         // one past the last key any column sees
-    int kv_len;          // rows at or beyond this key hold no data
+    const int32_t* bt;       // block-table row that holds the key range
+    int key_begin;           // first key; a multiple of the block size
+    int key_end;             // one past the last key any column sees
+    int kv_len;              // rows at or beyond this key hold no data
     int kvh;
-    const void* qptr;    // the lane's query elements 32 g .. 32 g + 31 (read only when cvalid)
-    bool cvalid;         // the lane's column exists
-    int cpos;            // last key the lane's column sees
-    bool wave_cols;      // the wave has at least one column
-    int wpos_min;        // smallest and largest last-visible key over the wave's columns
+    const void* qptr[CB];    // the lane's query elements 32 g .. 32 g + 31 (read only when cvalid)
+    bool cvalid[CB];         // the lane's column exists
+    int cpos[CB];            // last key the lane's column sees
+    bool wave_cols;          // the wave has at least one column
+    int wpos_min;            // smallest and largest last-visible key over the wave's columns
     int wpos_max;
 };
 
-// Runs the tile.  On return every lane holds its column's running max m (log2
-// units, uniform over the column's lanes), the sum l over all its lanes, and
-// the unnormalised accumulators acc[a][b][i] for dims 64 a + 16 g + 4 i + b;
-// `bad` is set when the table named a block outside the pool.  All threads of
-// the workgroup must call it.
-template <Fmt KV, int D, int BS, int G>
-__device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& m, float& l, f32x4 (&acc)[2][4],
-                        bool& bad) {
-    using Sh = MqShape<D, BS, G>;
+// Runs the tile.  On return every lane holds, for each column block cb, its
+// column's running max m[cb] (log2 units, uniform over the column's lanes),
+// the sum l[cb] over all its lanes, and the unnormalised accumulators
+// acc[cb][a][b][i] for dims 64 a + 16 g + 4 i + b; `bad` is set when the
+// table named a block outside the pool.  All threads of the workgroup must
+// call it.  STREAM marks the K/V copies non-temporal (data read once).
+template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM>
+__device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, float (&m)[CB], float (&l)[CB],
+                        f32x4 (&acc)[CB][2][4], bool& bad) {
+    using Sh = MqShape<D, BS, G, CB, STAGES>;
     using Ops = MfmaOps<KV>;
     using vec = typename Ops::vec;
-    constexpr int ROWB = Sh::ROWB, STEP = Sh::STEP, BPS = Sh::BPS, S = Sh::S;
+    constexpr int ROWB = Sh::ROWB, STEP = Sh::STEP, BPS = Sh::BPS, S = Sh::S, CPW = Sh::COPIES_PER_WAVE;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,17 +193,18 @@ __device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& 
     const int H = pool.num_kv_heads;
     const int kvh = t.kvh;
 
-    // ---- queries of this lane's column (zero for missing columns)
-    vec qop[4];
-    {
-        const u32x4* qp = (const u32x4*)t.qptr;
+    // ---- queries of this lane's columns (zero for missing columns)
+    vec qop[CB][4];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const u32x4* qp = (const u32x4*)t.qptr[cb];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const u32x4 v = t.cvalid ? qp[c] : u32x4{0, 0, 0, 0};
-            qop[c] = __builtin_bit_cast(vec, v);
+            const u32x4 v = t.cvalid[cb] ? qp[c] : u32x4{0, 0, 0, 0};
+            qop[cb][c] = __builtin_bit_cast(vec, v);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[c]));  // resident before the copies start
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[cb][c]));  // resident before the copies start
     }
 
     // ---- block ids of the key range into LDS, in windows of ID_CAP
@@ -194,94 +229,116 @@ __device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& 
     load_ids(0);
     __syncthreads();
 
-    // ---- copies of one step: wave w copies COPIES_PER_WAVE 1 KiB pieces;
-    // piece p < COPIES/2 is K, the rest V; each covers 4 rows of 256 bytes
-    const char* kc = (const char*)pool.k_cache;
-    const char* vc = (const char*)pool.v_cache;
+    // ---- copies of one step: wave w copies CPW 1 KiB pieces (waves 0 .. W/2-1
+    // the K pieces, the others the V pieces); each covers 4 rows of 256 bytes.
+    // Everything but the block id is fixed per lane and piece.
+    const bool wave_v = wave * CPW >= Sh::COPIES / 2;
+    const char* base = (const char*)(wave_v ? pool.v_cache : pool.k_cache);
+    const uint64_t block_bytes = (uint64_t)H * BS * ROWB;
     const uint32_t lds0 = lds_addr_of(smem);
+    uint32_t cp_dst[CPW];   // LDS offset inside a stage
+    uint32_t cp_src[CPW];   // byte offset inside a block
+    int cp_blk[CPW];        // block of the piece's row, relative to the step's first block
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int piece = wave * CPW + j;
+        const int pk = wave_v ? piece - Sh::COPIES / 2 : piece;
+        const int row = pk * 4 + lane / 16;   // key row inside the step
+        const int slot = lane % 16;           // 16-byte slot in the LDS row
+        const int gran = wave_v ? (slot ^ (((row >> 2) & 1) << 3)) : (slot ^ (row & 15));
+        cp_blk[j] = row / BS;
+        cp_src[j] = (uint32_t)(((kvh * BS) + row % BS) * ROWB + gran * 16);
+        cp_dst[j] = (uint32_t)((wave_v ? Sh::HALF : 0) + pk * 1024);
+    }
     auto issue = [&](int k, int stage) {
 #pragma unroll
-        for (int j = 0; j < Sh::COPIES_PER_WAVE; ++j) {
-            const int piece = wave * Sh::COPIES_PER_WAVE + j;
-            const bool is_v = piece >= Sh::COPIES / 2;
-            const int pk = is_v ? piece - Sh::COPIES / 2 : piece;
-            const int row = pk * 4 + lane / 16;                 // key row inside the step
-            const int slot = lane % 16;                          // 16-byte slot in the LDS row
-            const int gran = is_v ? (slot ^ (((row >> 2) & 1) << 3)) : (slot ^ (row & 15));
-            const int blk = k * BPS + row / BS;                  // block index relative to blk0
-            const int b0 = k * BPS;                              // the step's first block
-            const int use = blk < nblk ? blk : b0;               // past the last block: reread the first
-            const int pb = ids[use - window];
-            const size_t src = (((size_t)pb * H + kvh) * BS + row % BS) * ROWB + gran * 16;
-            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE + (is_v ? Sh::HALF : 0) + pk * 1024);
-            dma16_to_lds_stream((is_v ? vc : kc) + src, dst);
+        for (int j = 0; j < CPW; ++j) {
+            const int blk = k * BPS + cp_blk[j];
+            const int use = blk < nblk ? blk : k * BPS;  // past the last block: reread the step's first
+            const uint32_t pb = (uint32_t)ids[use - window];
+            const char* src = base + ((uint64_t)pb * block_bytes + cp_src[j]);
+            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE) + cp_dst[j];
+            if constexpr (STREAM)
+                dma16_to_lds_stream(src, dst);
+            else
+                dma16_to_lds(src, dst);
         }
     };
 
-    m = -INFINITY;
-    l = 0.f;
 #pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
+    for (int cb = 0; cb < CB; ++cb) {
+        m[cb] = -INFINITY;
+        l[cb] = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[aa][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[cb][aa][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const float qk_scale = pool.qk_scale_log2;
-    const int cpos = t.cvalid ? t.cpos : -1;  // missing columns see no key
+    int cpos[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) cpos[cb] = t.cvalid[cb] ? t.cpos[cb] : -1;  // missing columns see no key
 
     // LDS read offsets that do not depend on the step
     const int kslot[4] = {(4 * g + 0) ^ n, (4 * g + 1) ^ n, (4 * g + 2) ^ n, (4 * g + 3) ^ n};
 
-    auto step = [&](const char* st, int k0, auto masked) {
+    auto compute = [&](const char* st, int k0, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const char* kb = st;
         const char* vb = st + Sh::HALF;
-        // scores of both 16-key halves: sc[h][i] is key k0 + 16 h + 4 g + i
-        f32x4 sc[2];
+        // scores of both 16-key halves: sc[cb][h][i] is key k0 + 16 h + 4 g + i;
+        // each K operand serves every column block
+        f32x4 sc[CB][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const char* rowp = kb + (16 * h + n) * ROWB;
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-                c = Ops::mma(__builtin_bit_cast(vec, *(const u32x4*)(rowp + kslot[cc] * 16)), qop[cc], c);
-            sc[h] = c;
-        }
-        float s[2][4];
+            for (int h = 0; h < 2; ++h) sc[cb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = !MASKED || k0 + 16 * h + 4 * g + i <= cpos;
-                s[h][i] = ok ? sc[h][i] * qk_scale : -INFINITY;
+            for (int h = 0; h < 2; ++h) {
+                const vec ka = __builtin_bit_cast(vec, *(const u32x4*)(kb + (16 * h + n) * ROWB + kslot[cc] * 16));
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) sc[cb][h] = Ops::mma(ka, qop[cb][cc], sc[cb][h]);
             }
-        float mx = s[0][0];
+        vec phi[CB], plo[CB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int cb = 0; cb < CB; ++cb) {
+            float s[2][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[h][i]);
-        mx = mq_max_groups(mx);
-        const float mn = fmaxf(m, mx);
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {
-            const float alpha = fast_exp2(m - mu);
-            l *= alpha;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int aa = 0; aa < 2; ++aa)
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = !MASKED || k0 + 16 * h + 4 * g + i <= cpos[cb];
+                    s[h][i] = ok ? sc[cb][h][i] * qk_scale : -INFINITY;
+                }
+            float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            mx = mq_max_groups(mx);
+            const float mn = fmaxf(m[cb], mx);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            if (__builtin_amdgcn_ballot_w64(mn != m[cb]) != 0) {
+                const float alpha = fast_exp2(m[cb] - mu);
+                l[cb] *= alpha;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[aa][b] *= alpha;
-        }
-        m = mn;
-        vec phi, plo;
+                for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[h][i] - mu);
-                l += p;
-                const typename Ops::elem ph = (typename Ops::elem)p;
-                phi[4 * h + i] = ph;
-                plo[4 * h + i] = (typename Ops::elem)(p - (float)ph);
+                    for (int b = 0; b < 4; ++b) acc[cb][aa][b] *= alpha;
             }
-        // values: dims 64 a + 4 n + b of keys 16 h + 4 g + i, one product per (a, b)
+            m[cb] = mn;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = fast_exp2(s[h][i] - mu);
+                    l[cb] += p;
+                    const typename Ops::elem ph = (typename Ops::elem)p;
+                    phi[cb][4 * h + i] = ph;
+                    plo[cb][4 * h + i] = (typename Ops::elem)(p - (float)ph);
+                }
+        }
+        // values: dims 64 a + 4 n + b of keys 16 h + 4 g + i, one operand per
+        // (a, b), used by every column block
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
             u32x2 w[2][4];
@@ -296,7 +353,7 @@ __device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& 
                         if (k0 + row >= t.kv_len) w[h][i] = u32x2{0u, 0u};  // rows past the data may hold anything
                     }
                 }
-            // operand b, element 4 h + i = element b of w[h][i]: pairs of keys
+            // operand element 4 h + i = element b of w[h][i]: pairs of keys
             // share a 32-bit word
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -311,33 +368,31 @@ __device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& 
                         op[2 * h + ip] = __builtin_amdgcn_perm(hi, lo, sel);
                     }
                 const vec A = __builtin_bit_cast(vec, op);
-                acc[aa][b] = Ops::mma(A, phi, acc[aa][b]);
-                acc[aa][b] = Ops::mma(A, plo, acc[aa][b]);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    acc[cb][aa][b] = Ops::mma(A, phi[cb], acc[cb][aa][b]);
+                    acc[cb][aa][b] = Ops::mma(A, plo[cb], acc[cb][aa][b]);
+                }
             }
         }
     };
 
     // ---- main loop over 32-key steps, S - 1 steps of copies ahead.  The
     // first S - 1 steps never need a new id window (S - 1 < ID_CAP / BPS).
+    // Steps before k_plain need no mask for any column of this wave (all
+    // their keys are visible and hold data); the two loops below differ
+    // only in that, and in skipping steps after the wave's last visible key.
     const int nsteps = (t.key_end - t.key_begin + STEP - 1) / STEP;
     const int steps_per_window = Sh::ID_CAP / BPS;
+    const int lim = min(t.wpos_min + 1, t.kv_len) - t.key_begin;
+    const int k_plain = __builtin_amdgcn_readfirstlane(t.wave_cols ? min(max(lim, 0) / STEP, nsteps) : 0);
 #pragma unroll
     for (int k = 0; k < S - 1; ++k)
         if (k < nsteps) issue(k, k);
-    for (int k = 0; k < nsteps; ++k) {
+    auto advance = [&](int k) {
         // this wave's copies of step k are complete when at most those of the
         // later steps already issued (up to S - 2 of them) are in flight
-        const int later = min(S - 2, nsteps - 1 - k);
-        if constexpr (S >= 4) {
-            if (later >= 2) wait_vmcnt<2 * Sh::COPIES_PER_WAVE>();
-            else if (later == 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
-            else wait_vmcnt<0>();
-        } else if constexpr (S == 3) {
-            if (later >= 1) wait_vmcnt<Sh::COPIES_PER_WAVE>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_later_steps<CPW, S - 2>(min(S - 2, nsteps - 1 - k));
         __syncthreads();  // everyone's copies of step k landed; step k-1 is finished everywhere
         const int kn = k + S - 1;  // the step whose copies go out now, into step k-1's stage
         if (kn < nsteps) {
@@ -348,16 +403,19 @@ __device__ void mq_tile(const MqPool& pool, const MqTask& t, char* smem, float& 
             }
             issue(kn, kn % S);
         }
-        const int k0 = t.key_begin + k * STEP;
-        if (t.wave_cols && k0 <= t.wpos_max) {  // some column of this wave sees keys of this step
-            const char* st = smem + (k % S) * Sh::STAGE;
-            if (k0 + STEP - 1 <= t.wpos_min && k0 + STEP <= t.kv_len)
-                step(st, k0, std::false_type{});
-            else
-                step(st, k0, std::true_type{});
-        }
+    };
+    for (int k = 0; k < k_plain; ++k) {
+        advance(k);
+        compute(smem + (k % S) * Sh::STAGE, t.key_begin + k * STEP, std::false_type{});
     }
-    l = mq_sum_groups(l);
+    for (int k = k_plain; k < nsteps; ++k) {
+        advance(k);
+        const int k0 = t.key_begin + k * STEP;
+        if (t.wave_cols && k0 <= t.wpos_max)  // some column of this wave sees keys of this step
+            compute(smem + (k % S) * Sh::STAGE, k0, std::true_type{});
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) l[cb] = mq_sum_groups(l[cb]);
     bad = *bad_flag != 0;
 }
 

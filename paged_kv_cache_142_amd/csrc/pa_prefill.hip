@@ -5,18 +5,36 @@
 // query_start[i] packed query rows are its last Q tokens (row j at position
 // T - Q + j) and each attends to the cached tokens 0 .. its position.
 //
-// Work decomposition: one workgroup per (sequence, query tile, kv head).  A
-// tile holds TQ = 64 / G query tokens, i.e. 64 (token, query head) columns
-// for the G query heads of the kv head; each of the four waves owns 16 of
-// them.  The workgroup runs the multi-query tile of pa_mq_mfma.hpp over the
-// keys 0 .. (its last position); column (token at position p) sees keys
-// 0 .. p.
+// Work decomposition: one workgroup per (query tile, kv head).  A tile holds
+// TQ = 128 / G query tokens of one sequence, i.e. 128 (token, query head)
+// columns for the G query heads of the kv head; each of the four waves owns
+// 32 of them (two column blocks of 16).  The workgroup runs the multi-query
+// tile of pa_mq_mfma.hpp over the keys 0 .. (its last position); column
+// (token at position p) sees keys 0 .. p.  The K/V copies keep the cache
+// hint: every tile of a sequence reads its keys again.
+//
+// The grid holds only real tiles (at most total_q / TQ + num_seqs of them):
+// each workgroup finds its tile from the query counts, in the order "highest
+// tile index first" (tile j of a full prefill sees (j + 1) TQ keys, so this is
+// longest-first), sequences in index order within an index.  Launching a
+// grid sized for max_query_len instead leaves most workgroups of the early
+// (high) tile indices empty, and those hold dispatch slots while the long
+// tiles wait.
 //
 // A block id outside the pool makes the tile's output rows NaN (the tile
 // never uses it as an address); so does an invalid sequence length.
 #include "pa_mq_mfma.hpp"
 
+#ifndef PA_PREFILL_CB
+#define PA_PREFILL_CB 2
+#endif
+#ifndef PA_PREFILL_STREAM
+#define PA_PREFILL_STREAM false
+#endif
+
 namespace pa {
+
+constexpr int PREFILL_CB = PA_PREFILL_CB;
 
 struct PrefillArgs {
     void* out;
@@ -31,12 +49,65 @@ struct PrefillArgs {
     int max_seq_len;
     int num_seqs;
     int num_heads;
-    int tiles;  // query tiles per sequence in the grid
+    int tiles;  // upper bound of the query tiles of one sequence
 };
+
+// Tiles of sequence i (0 past the last sequence or for rows that cannot be
+// addressed).
+template <int TQ>
+__device__ __forceinline__ int prefill_tiles_of(const PrefillArgs& a, int i) {
+    if (i >= a.num_seqs) return 0;
+    const int q0 = a.query_start[i];
+    const int q1 = a.query_start[i + 1];
+    if (q0 < 0 || q1 < q0 || q1 > a.total_q) return 0;
+    return (q1 - q0 + TQ - 1) / TQ;
+}
+
+// The p-th tile of the order "highest tile index first, then sequence
+// index", computed by one wavefront (sequences spread over the lanes in
+// chunks of 64).  With c(j) = sum_i max(tiles_i - j, 0), the items of tile
+// index j are c(j+1) .. c(j) - 1: a binary search on j, then the r-th
+// sequence (in index order) that has more than j tiles.
+template <int TQ>
+__device__ bool prefill_item(const PrefillArgs& a, int p, int& seq, int& tile) {
+    const int lane = threadIdx.x & 63;
+    const int t0 = prefill_tiles_of<TQ>(a, lane);  // the first chunk stays in a register
+    auto count_from = [&](int j) {                  // c(j), uniform
+        int x = max(t0 - j, 0);
+        for (int c = 64; c < a.num_seqs; c += 64) x += max(prefill_tiles_of<TQ>(a, c + lane) - j, 0);
+        return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63);
+    };
+    if (p >= count_from(0)) return false;
+    int lo = 0, hi = a.tiles;  // c(lo) > p >= c(hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (count_from(mid) > p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    int r = p - count_from(lo + 1);
+    for (int c = 0; c < a.num_seqs; c += 64) {
+        const bool has = (c == 0 ? t0 : prefill_tiles_of<TQ>(a, c + lane)) > lo;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+        const int cnt = __builtin_popcountll(m);
+        if (r < cnt) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
+            if (hit == 0) return false;  // cannot happen for r < cnt
+            seq = c + __builtin_ctzll(hit);
+            tile = lo;
+            return true;
+        }
+        r -= cnt;
+    }
+    return false;
+}
+
 
 template <Fmt KV, int D, int BS, int G>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs a) {
-    using Sh = MqShape<D, BS, G>;
+    using Sh = MqShape<D, BS, G, PREFILL_CB>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
@@ -44,14 +115,11 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     const int g = lane >> 4;
     const int n = lane & 15;
 
-    // ---- (sequence, tile, kv head) of this workgroup: the last tiles of the
-    // chunks first, since they see the most keys
+    // ---- (sequence, tile, kv head) of this workgroup
     const int H = a.pool.num_kv_heads;
-    const int per_tile = a.num_seqs * H;
-    const int tile = a.tiles - 1 - (int)(blockIdx.x / per_tile);
-    const int rem = blockIdx.x % per_tile;
-    const int seq = rem / H;
-    const int kvh = rem - seq * H;
+    const int kvh = (int)(blockIdx.x % H);
+    int seq, tile;
+    if (!prefill_item<Sh::TQ>(a, (int)(blockIdx.x / H), seq, tile)) return;
 
     const int q0 = a.query_start[seq];
     const int q1 = a.query_start[seq + 1];
@@ -73,53 +141,61 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
         return;
     }
 
-    // this lane's column: token tok_lo + wave * (16 / G) + n / G, head n % G
-    MqTask t;
-    const int ctok = tok_lo + wave * Sh::PER_WAVE + n / G;
+    // this lane's column in block cb: token tok_lo + wave * PER_WAVE +
+    // (16 cb + n) / G, head n % G
+    MqTask<PREFILL_CB> t;
     const int chead = kvh * G + n % G;
+    int ctok[PREFILL_CB];
     t.bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq;
     t.key_begin = 0;
     t.key_end = T - Q + tok_hi;  // one past the last position of the tile
     t.kv_len = T;
     t.kvh = kvh;
-    t.cvalid = ctok < tok_hi;
-    t.cpos = T - Q + ctok;
-    t.qptr = (const char*)a.q + (((size_t)(q0 + (t.cvalid ? ctok : tok_lo)) * a.num_heads + chead) * D + 32 * g) * 2;
+#pragma unroll
+    for (int cb = 0; cb < PREFILL_CB; ++cb) {
+        ctok[cb] = tok_lo + wave * Sh::PER_WAVE + (16 * cb + n) / G;
+        t.cvalid[cb] = ctok[cb] < tok_hi;
+        t.cpos[cb] = T - Q + ctok[cb];
+        t.qptr[cb] = (const char*)a.q +
+                     (((size_t)(q0 + (t.cvalid[cb] ? ctok[cb] : tok_lo)) * a.num_heads + chead) * D + 32 * g) * 2;
+    }
     const int wtok_lo = tok_lo + wave * Sh::PER_WAVE;
     const int wtok_hi = min(wtok_lo + Sh::PER_WAVE, tok_hi);
     t.wave_cols = wtok_lo < tok_hi;
     t.wpos_min = T - Q + wtok_lo;
     t.wpos_max = T - Q + wtok_hi - 1;
 
-    float m, l;
-    f32x4 acc[2][4];
+    float m[PREFILL_CB], l[PREFILL_CB];
+    f32x4 acc[PREFILL_CB][2][4];
     bool bad;
-    mq_tile<KV, D, BS, G>(a.pool, t, smem, m, l, acc, bad);
+    mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM>(a.pool, t, smem, m, l, acc, bad);
 
-    // ---- output: column n, dims 64 a + 16 g + 4 i + b
-    if (t.cvalid) {
-        const float inv = 1.f / l;
-        const size_t base = ((size_t)(q0 + ctok) * a.num_heads + chead) * D;
+    // ---- output: column n of each block, dims 64 a + 16 g + 4 i + b, four
+    // consecutive dims (b = 0..3) per store
+#pragma unroll
+    for (int cb = 0; cb < PREFILL_CB; ++cb) {
+        if (!t.cvalid[cb]) continue;
+        const float inv = bad ? __builtin_nanf("") : 1.f / l[cb];
+        const size_t base = ((size_t)(q0 + ctok[cb]) * a.num_heads + chead) * D;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float v = bad ? __builtin_nanf("") : acc[aa][b][i] * inv;
-                    store_out(a.out, a.out_dtype, base + 64 * aa + 16 * g + 4 * i + b, v);
-                }
+                store_out4(a.out, a.out_dtype, base + 64 * aa + 16 * g + 4 * i,
+                           f32x4{acc[cb][aa][0][i], acc[cb][aa][1][i], acc[cb][aa][2][i], acc[cb][aa][3][i]} * inv);
     }
 }
 
 template <Fmt KV, int D, int BS, int G>
 static int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    using Sh = MqShape<D, BS, G>;
+    using Sh = MqShape<D, BS, G, PREFILL_CB>;
     auto kernel = prefill_mfma_kernel<KV, D, BS, G>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const size_t grid = (size_t)a.tiles * a.num_seqs * a.pool.num_kv_heads;
+    // every real tile: at most total_q / TQ + num_seqs of them
+    const size_t items = (size_t)(a.total_q + Sh::TQ - 1) / Sh::TQ + (size_t)a.num_seqs;
+    const size_t grid = items * a.pool.num_kv_heads;
     if (grid == 0) return PA_OK;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -129,10 +205,10 @@ template <Fmt KV, int D, int BS>
 static int dispatch_prefill_group(PrefillArgs& a, int group, int max_query_len, hipStream_t stream) {
     auto tiles = [&](int tq) { return (max_query_len + tq - 1) / tq; };
     switch (group) {
-        case 1: a.tiles = tiles(MqShape<D, BS, 1>::TQ); return launch_prefill<KV, D, BS, 1>(a, stream);
-        case 2: a.tiles = tiles(MqShape<D, BS, 2>::TQ); return launch_prefill<KV, D, BS, 2>(a, stream);
-        case 4: a.tiles = tiles(MqShape<D, BS, 4>::TQ); return launch_prefill<KV, D, BS, 4>(a, stream);
-        case 8: a.tiles = tiles(MqShape<D, BS, 8>::TQ); return launch_prefill<KV, D, BS, 8>(a, stream);
+        case 1: a.tiles = tiles(MqShape<D, BS, 1, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 1>(a, stream);
+        case 2: a.tiles = tiles(MqShape<D, BS, 2, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 2>(a, stream);
+        case 4: a.tiles = tiles(MqShape<D, BS, 4, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 4>(a, stream);
+        case 8: a.tiles = tiles(MqShape<D, BS, 8, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 8>(a, stream);
     }
     return PA_ERR_UNSUPPORTED;
 }
@@ -164,9 +240,9 @@ extern "C" int pa_prefill(void* out, int out_dtype, const void* q, int q_dtype, 
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || total_q == 0 || max_query_len == 0) return PA_OK;
     if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL;
-    if ((((uintptr_t)q) | ((uintptr_t)k_cache) | ((uintptr_t)v_cache)) & 15u) return PA_ERR_SHAPE;
-    const long long tiles_max = (max_query_len + 7) / 8;  // the smallest tile is 8 tokens
-    if (tiles_max * num_seqs * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if ((((uintptr_t)out) | ((uintptr_t)q) | ((uintptr_t)k_cache) | ((uintptr_t)v_cache)) & 15u) return PA_ERR_SHAPE;
+    const long long items_max = (total_q + 7) / 8 + (long long)num_seqs;  // the smallest tile is 8 tokens
+    if (items_max * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
     PrefillArgs a;
     a.out = out;
     a.out_dtype = out_dtype;

@@ -232,3 +232,5 @@ def test_prefill_validation(lib):
     for ptr in ("out", "q", "qs", "kc", "vc", "bt", "lens"):
         assert _pf(lib, **{ptr: None}) == NULL
     assert _pf(lib, q=FAKE + 4) == SHAPE        # not 16-byte aligned
+    assert _pf(lib, out=FAKE + 8) == SHAPE      # output rows are written 16 bytes at a time
+    assert _pf(lib, total_q=(1 << 31) - 8, mql=64, kvh=64, heads=64) == SHAPE  # grid beyond 2^31 workgroups

@@ -8,7 +8,9 @@
 // are walked in steps of 32 (two blocks of 16 or one of 32): the step's K and
 // V rows are copied once into LDS (the four waves issue a quarter of the
 // 16-byte asynchronous copies each) and serve all the columns; inside a wave
-// each K and V operand read from LDS serves its CB column blocks.  An S-stage ring keeps S - 1 steps of
+// each K and V operand read from LDS serves its CB column blocks.  An
+// S-stage ring holds the two steps being computed (the score products of
+// step k + 1 run beside the value products of step k) and S - 2 steps of
 // copies in flight; one barrier per step separates "everyone finished step
 // k-1" from "step k+S-1 may overwrite its stage".
 //
@@ -20,8 +22,10 @@
 //            lane receives column n's scores for keys 4 g + i, i = 0..3, of
 //            each half.
 //   softmax  per column: the lane's 8 scores, a max across the four lane
-//            groups, the running max uniform over the column's lanes; keys
-//            after the column's last visible position get -inf.
+//            groups, a reference maximum uniform over the column's lanes
+//            that moves (rescaling the accumulators) only when the running
+//            maximum passes it by more than MQ_SLACK; keys after the
+//            column's last visible position get weight 0.
 //   values   O^T[dim][column] += V^T P^T: B = the lane's own p (split into
 //            a 16-bit high part and the rounded remainder, two products, so
 //            p keeps about 16 significant bits); A = V^T, the lane supplying
@@ -53,27 +57,59 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <Fmt F> struct MfmaOps;
 template <> struct MfmaOps<Fmt::BF16> {
     typedef bf16x8 vec;
-    typedef __bf16 elem;
+    typedef bf16x2 pair;
     __device__ static __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 template <> struct MfmaOps<Fmt::F16> {
     typedef f16x8 vec;
-    typedef _Float16 elem;
+    typedef f16x2 pair;
     __device__ static __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
 };
 
+// Two-part 16-bit form of 8 weights: hi = round(p), lo = round(p - hi), so
+// that hi + lo keeps about 16 significant bits of p.  Pairs are converted
+// together (one packed conversion each for hi and lo).
+template <Fmt KV>
+__device__ __forceinline__ void mq_split8(const float (&p)[8], typename MfmaOps<KV>::vec& hi,
+                                          typename MfmaOps<KV>::vec& lo) {
+    using pair = typename MfmaOps<KV>::pair;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const pair h = __builtin_convertvector(f32x2{p[e], p[e + 1]}, pair);
+        const f32x2 hf = __builtin_convertvector(h, f32x2);
+        const pair r = __builtin_convertvector(f32x2{p[e] - hf[0], p[e + 1] - hf[1]}, pair);
+        hi[e] = h[0];
+        hi[e + 1] = h[1];
+        lo[e] = r[0];
+        lo[e + 1] = r[1];
+    }
+}
+
+// Maxima as single instructions (no NaN canonicalisation of the operands:
+// the scores come from the matrix cores and are never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Maximum and sum over the four 16-lane groups (lanes n, n+16, n+32, n+48).
 __device__ __forceinline__ float mq_max_groups(float x) {
     const uint32_t u = __float_as_uint(x);
     const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float y = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const uint32_t v = __float_as_uint(y);
     const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float mq_sum_groups(float x) {
@@ -115,8 +151,14 @@ struct MqShape {
     static_assert(COPIES % W == 0 && COPIES / 2 % COPIES_PER_WAVE == 0, "a wave copies only K or only V");
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
-    static_assert(S >= 2 && (S - 2) * COPIES_PER_WAVE <= 63, "vmcnt holds the copies of S - 2 steps");
+    static_assert(S >= 3, "two resident steps (the pipelined loop) plus one being refilled");
+    static_assert((S - 2) * COPIES_PER_WAVE <= 63, "vmcnt holds the copies of S - 2 steps");
 };
+
+// How far (log2 units) a column's running maximum may rise above the
+// reference its weights are taken against before the reference is moved and
+// the accumulators rescaled: weights stay below 2^8, far from float overflow.
+constexpr float MQ_SLACK = 8.f;
 
 // Waits until at most `later` (< N + 1) steps of C copies each, issued after
 // the one needed now, are still in flight.
@@ -173,9 +215,12 @@ struct MqTask {
 };
 
 // Runs the tile.  On return every lane holds, for each column block cb, its
-// column's running max m[cb] (log2 units, uniform over the column's lanes),
-// the sum l[cb] over all its lanes, and the unnormalised accumulators
-// acc[cb][a][b][i] for dims 64 a + 16 g + 4 i + b; `bad` is set when the
+// column's reference m[cb] (log2 units, uniform over the column's lanes; at
+// most MQ_SLACK below the column's largest scaled score, -inf if it saw no
+// key), the sum l[cb] = sum 2^(c s - m) over all its keys, and the
+// unnormalised accumulators acc[cb][a][b][i] = sum 2^(c s - m) v for dims
+// 64 a + 16 g + 4 i + b, so that (m, l, acc) is a partition state in the
+// decode kernels' sense; `bad` is set when the
 // table named a block outside the pool.  All threads of the workgroup must
 // call it.  STREAM marks the K/V copies non-temporal (data read once).
 template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM>
@@ -193,14 +238,18 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     const int H = pool.num_kv_heads;
     const int kvh = t.kvh;
 
-    // ---- queries of this lane's columns (zero for missing columns)
+    // ---- queries of this lane's columns (zero for missing columns).  A
+    // negative score scale is moved into the queries (an exact sign flip), so
+    // that the scale c applied below is never negative and max(c s) = c max(s).
+    const uint32_t qsign = pool.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
+    const float c_scale = fabsf(pool.qk_scale_log2);
     vec qop[CB][4];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const u32x4* qp = (const u32x4*)t.qptr[cb];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const u32x4 v = t.cvalid[cb] ? qp[c] : u32x4{0, 0, 0, 0};
+            const u32x4 v = t.cvalid[cb] ? (qp[c] ^ qsign) : u32x4{0, 0, 0, 0};
             qop[cb][c] = __builtin_bit_cast(vec, v);
         }
 #pragma unroll
@@ -233,12 +282,10 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     // the K pieces, the others the V pieces); each covers 4 rows of 256 bytes.
     // Everything but the block id is fixed per lane and piece.
     const bool wave_v = wave * CPW >= Sh::COPIES / 2;
-    const char* base = (const char*)(wave_v ? pool.v_cache : pool.k_cache);
-    const uint64_t block_bytes = (uint64_t)H * BS * ROWB;
+    const uint32_t block_bytes = (uint32_t)H * BS * ROWB;
     const uint32_t lds0 = lds_addr_of(smem);
-    uint32_t cp_dst[CPW];   // LDS offset inside a stage
-    uint32_t cp_src[CPW];   // byte offset inside a block
-    int cp_blk[CPW];        // block of the piece's row, relative to the step's first block
+    const char* cp_base[CPW];  // the piece's row and granule in block 0 of the pool
+    int cp_blk[CPW];           // block of the piece's row, relative to the step's first block
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
         const int piece = wave * CPW + j;
@@ -247,17 +294,22 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
         const int slot = lane % 16;           // 16-byte slot in the LDS row
         const int gran = wave_v ? (slot ^ (((row >> 2) & 1) << 3)) : (slot ^ (row & 15));
         cp_blk[j] = row / BS;
-        cp_src[j] = (uint32_t)(((kvh * BS) + row % BS) * ROWB + gran * 16);
-        cp_dst[j] = (uint32_t)((wave_v ? Sh::HALF : 0) + pk * 1024);
+        cp_base[j] = (const char*)(wave_v ? pool.v_cache : pool.k_cache) + ((kvh * BS) + row % BS) * ROWB + gran * 16;
     }
+    // LDS offset of piece j inside a stage (uniform)
+    auto cp_dst = [&](int j) {
+        const int piece = wave * CPW + j;
+        return (uint32_t)((wave_v ? Sh::HALF : 0) + (wave_v ? piece - Sh::COPIES / 2 : piece) * 1024);
+    };
     auto issue = [&](int k, int stage) {
+        const int b0 = k * BPS - window;                              // the step's first block in `ids`
+        const bool whole = k * BPS + BPS <= nblk;                     // uniform: every block of the step exists
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int blk = k * BPS + cp_blk[j];
-            const int use = blk < nblk ? blk : k * BPS;  // past the last block: reread the step's first
-            const uint32_t pb = (uint32_t)ids[use - window];
-            const char* src = base + ((uint64_t)pb * block_bytes + cp_src[j]);
-            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE) + cp_dst[j];
+            const int use = (whole || k * BPS + cp_blk[j] < nblk) ? b0 + cp_blk[j] : b0;  // else reread the first
+            const uint32_t pb = (uint32_t)ids[use];
+            const char* src = cp_base[j] + (uint64_t)pb * block_bytes;
+            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE) + cp_dst(j);
             if constexpr (STREAM)
                 dma16_to_lds_stream(src, dst);
             else
@@ -274,7 +326,6 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[cb][aa][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float qk_scale = pool.qk_scale_log2;
     int cpos[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) cpos[cb] = t.cvalid[cb] ? t.cpos[cb] : -1;  // missing columns see no key
@@ -282,13 +333,13 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     // LDS read offsets that do not depend on the step
     const int kslot[4] = {(4 * g + 0) ^ n, (4 * g + 1) ^ n, (4 * g + 2) ^ n, (4 * g + 3) ^ n};
 
-    auto compute = [&](const char* st, int k0, auto masked) {
-        constexpr bool MASKED = decltype(masked)::value;
-        const char* kb = st;
-        const char* vb = st + Sh::HALF;
-        // scores of both 16-key halves: sc[cb][h][i] is key k0 + 16 h + 4 g + i;
-        // each K operand serves every column block
-        f32x4 sc[CB][2];
+    auto stage_of = [&](int k) { return smem + (k % S) * Sh::STAGE; };
+
+    // scores of step k, both 16-key halves: sc[cb][h][i] is key k0 + 16 h +
+    // 4 g + i; each K operand read from LDS serves every column block
+    f32x4 sc[CB][2];
+    auto qk = [&](int k) {
+        const char* kb = stage_of(k);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -301,44 +352,64 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) sc[cb][h] = Ops::mma(ka, qop[cb][cc], sc[cb][h]);
             }
-        vec phi[CB], plo[CB];
+    };
+
+    // Weights of step k from its scores.  Online softmax with a lazily moved
+    // reference: p = 2^(c s - m) against the column's reference m, which
+    // moves to the running maximum only when that exceeds m by more than
+    // MQ_SLACK (so p <= 2^MQ_SLACK); l and acc always refer to the current m.
+    // The common path computes p against the current m without waiting for
+    // the maximum; the rare move recomputes them.
+    vec phi[CB], plo[CB];
+    auto softmax = [&](int k, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int k0 = t.key_begin + k * STEP;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            float s[2][4];
+            bool ok[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = !MASKED || k0 + 16 * h + 4 * g + i <= cpos[cb];
-                    s[h][i] = ok ? sc[cb][h][i] * qk_scale : -INFINITY;
-                }
-            float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                for (int i = 0; i < 4; ++i) ok[h][i] = !MASKED || k0 + 16 * h + 4 * g + i <= cpos[cb];
+            auto mval = [&](int h, int i) { return ok[h][i] ? sc[cb][h][i] : -INFINITY; };
+            auto weights = [&](float nmu) {
+                float p[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[4 * h + i] = fast_exp2(fmaf(sc[cb][h][i], c_scale, nmu));
+                        if constexpr (MASKED) p[4 * h + i] = ok[h][i] ? p[4 * h + i] : 0.f;
+                    }
+                mq_split8<KV>(p, phi[cb], plo[cb]);
+                return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            };
+            const float l0 = l[cb];
+            l[cb] = l0 + weights(m[cb] == -INFINITY ? 0.f : -m[cb]);
+            float mx = max3f(max3f(mval(0, 0), mval(0, 1), mval(0, 2)), max3f(mval(0, 3), mval(1, 0), mval(1, 1)),
+                             max3f(mval(1, 2), mval(1, 3), -INFINITY));
             mx = mq_max_groups(mx);
-            const float mn = fmaxf(m[cb], mx);
-            const float mu = mn == -INFINITY ? 0.f : mn;
-            if (__builtin_amdgcn_ballot_w64(mn != m[cb]) != 0) {
+            const float mxs = mx == -INFINITY ? -INFINITY : mx * c_scale;  // c >= 0: max of the scaled scores
+            if (__builtin_amdgcn_ballot_w64(mxs > m[cb] + MQ_SLACK) != 0) {
+                const float mn = fmaxf(m[cb], mxs);
+                const float mu = mn == -INFINITY ? 0.f : mn;
                 const float alpha = fast_exp2(m[cb] - mu);
-                l[cb] *= alpha;
 #pragma unroll
                 for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) acc[cb][aa][b] *= alpha;
+                m[cb] = mn;
+                l[cb] = l0 * alpha + weights(-mu);
             }
-            m[cb] = mn;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(s[h][i] - mu);
-                    l[cb] += p;
-                    const typename Ops::elem ph = (typename Ops::elem)p;
-                    phi[cb][4 * h + i] = ph;
-                    plo[cb][4 * h + i] = (typename Ops::elem)(p - (float)ph);
-                }
         }
-        // values: dims 64 a + 4 n + b of keys 16 h + 4 g + i, one operand per
-        // (a, b), used by every column block
+    };
+
+    // acc += V^T P^T for step k: dims 64 a + 4 n + b of keys 16 h + 4 g + i,
+    // one operand per (a, b), used by every column block
+    auto pv = [&](int k, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int k0 = t.key_begin + k * STEP;
+        const char* vb = stage_of(k) + Sh::HALF;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa) {
             u32x2 w[2][4];
@@ -377,24 +448,33 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
         }
     };
 
-    // ---- main loop over 32-key steps, S - 1 steps of copies ahead.  The
+    // ---- main loop over 32-key steps, software pipelined: iteration k
+    // issues the score products of step k + 1 and the value products of
+    // step k, then turns step k + 1's scores into weights while those run.
+    // Steps k and k + 1 are resident (S - 2 steps of copies in flight); the
     // first S - 1 steps never need a new id window (S - 1 < ID_CAP / BPS).
     // Steps before k_plain need no mask for any column of this wave (all
-    // their keys are visible and hold data); the two loops below differ
-    // only in that, and in skipping steps after the wave's last visible key.
+    // their keys are visible and hold data); steps from k_vis on hold no key
+    // any column of the wave sees.
     const int nsteps = (t.key_end - t.key_begin + STEP - 1) / STEP;
     const int steps_per_window = Sh::ID_CAP / BPS;
     const int lim = min(t.wpos_min + 1, t.kv_len) - t.key_begin;
     const int k_plain = __builtin_amdgcn_readfirstlane(t.wave_cols ? min(max(lim, 0) / STEP, nsteps) : 0);
+    const int vis = t.wpos_max - t.key_begin;
+    const int k_vis = __builtin_amdgcn_readfirstlane(t.wave_cols && vis >= 0 ? min(vis / STEP + 1, nsteps) : 0);
 #pragma unroll
     for (int k = 0; k < S - 1; ++k)
         if (k < nsteps) issue(k, k);
+    // wait until this wave's copies of steps <= `need` are complete, then
+    // the barrier: everyone's copies up to `need` landed
+    auto landed = [&](int need) {
+        const int issued = min(need == 0 ? S - 2 : need + S - 3, nsteps - 1);  // last step issued so far
+        wait_later_steps<CPW, S - 2>(issued - need);
+        __syncthreads();
+    };
     auto advance = [&](int k) {
-        // this wave's copies of step k are complete when at most those of the
-        // later steps already issued (up to S - 2 of them) are in flight
-        wait_later_steps<CPW, S - 2>(min(S - 2, nsteps - 1 - k));
-        __syncthreads();  // everyone's copies of step k landed; step k-1 is finished everywhere
-        const int kn = k + S - 1;  // the step whose copies go out now, into step k-1's stage
+        landed(min(k + 1, nsteps - 1));  // steps k and k + 1; step k - 1 is finished everywhere
+        const int kn = k + S - 1;        // the step whose copies go out now, into step k-1's stage
         if (kn < nsteps) {
             if (kn % steps_per_window == 0) {  // its ids are in the next window
                 window = kn * BPS;
@@ -404,15 +484,35 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
             issue(kn, kn % S);
         }
     };
-    for (int k = 0; k < k_plain; ++k) {
-        advance(k);
-        compute(smem + (k % S) * Sh::STAGE, t.key_begin + k * STEP, std::false_type{});
+    if (nsteps > 0) {
+        landed(0);
+        if (k_vis > 0) {
+            qk(0);
+            if (k_plain > 0)
+                softmax(0, std::false_type{});
+            else
+                softmax(0, std::true_type{});
+        }
     }
-    for (int k = k_plain; k < nsteps; ++k) {
+    int k = 0;
+    for (; k + 1 < k_plain; ++k) {  // steps k and k + 1 plain
         advance(k);
-        const int k0 = t.key_begin + k * STEP;
-        if (t.wave_cols && k0 <= t.wpos_max)  // some column of this wave sees keys of this step
-            compute(smem + (k % S) * Sh::STAGE, k0, std::true_type{});
+        qk(k + 1);
+        pv(k, std::false_type{});
+        softmax(k + 1, std::false_type{});
+    }
+    if (k < k_plain) {  // step k plain, k + 1 masked (or past the wave's keys)
+        advance(k);
+        if (k + 1 < k_vis) qk(k + 1);
+        pv(k, std::false_type{});
+        if (k + 1 < k_vis) softmax(k + 1, std::true_type{});
+        ++k;
+    }
+    for (; k < nsteps; ++k) {
+        advance(k);
+        if (k + 1 < k_vis) qk(k + 1);
+        if (k < k_vis) pv(k, std::true_type{});
+        if (k + 1 < k_vis) softmax(k + 1, std::true_type{});
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) l[cb] = mq_sum_groups(l[cb]);

@@ -118,15 +118,14 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
     if (!t.cvalid[0]) return;
     const size_t row = (size_t)seq * d.num_heads + head;
     const float nan = __builtin_nanf("");
-    // four consecutive dims (b = 0..3) per store
+    // dims 64 a + 16 b + 4 g + i: four consecutive dims (i = 0..3) per store
     if ((T + P - 1) / P == 1) {  // the sequence is this one shared partition: finish its row
         const float inv = bad ? nan : 1.f / l;
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                store_out4(d.out, d.out_dtype, row * D + 64 * aa + 16 * g + 4 * i,
-                           f32x4{acc[aa][0][i], acc[aa][1][i], acc[aa][2][i], acc[aa][3][i]} * inv);
+            for (int b = 0; b < 4; ++b)
+                store_out4(d.out, d.out_dtype, row * D + 64 * aa + 16 * b + 4 * g, acc[aa][b] * inv);
         return;
     }
     const size_t pidx = row * d.max_partitions + part;
@@ -138,9 +137,8 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_nontemporal_store(f32x4{acc[aa][0][i], acc[aa][1][i], acc[aa][2][i], acc[aa][3][i]} * one,
-                                        (f32x4*)&d.part_acc[pidx * D + 64 * aa + 16 * g + 4 * i]);
+        for (int b = 0; b < 4; ++b)
+            __builtin_nontemporal_store(acc[aa][b] * one, (f32x4*)&d.part_acc[pidx * D + 64 * aa + 16 * b + 4 * g]);
 }
 
 template <Fmt KV, int D, int BS, int G>

@@ -29,13 +29,14 @@
 //   values   O^T[dim][column] += V^T P^T: B = the lane's own p (split into
 //            a 16-bit high part and the rounded remainder, two products, so
 //            p keeps about 16 significant bits); A = V^T, the lane supplying
-//            dims 64 a + 4 n + b of its 8 keys (eight 8-byte LDS reads
-//            repacked by byte permutes, one product per (a, b)).  The lane
-//            receives column n's dims 64 a + 16 g + 4 i + b.
+//            dim 16 j + n of its 8 keys, delivered in that order by two
+//            transposing LDS reads per 16-dim block j.  The lane receives
+//            column n's dims 16 j + 4 g + i.
 // K rows sit in LDS XOR-swizzled by 16-byte granule (row t, granule x at
-// slot x ^ (t mod 16)) and V rows by half row (x ^ 8 when bit 2 of t is
-// set), both through the copies' source addresses, so that the reads above
-// spread over the banks.
+// slot x ^ (t mod 16)) and V rows by pairs of granules (x ^ 2 (t mod 8)),
+// both through the copies' source addresses, so that the reads above spread
+// over the banks (a transposing read touches one 32-byte dim block of 16
+// rows, whose t mod 8 take every value twice).
 //
 // The physical block ids of the key range are loaded into LDS first (in
 // windows of ID_CAP blocks).  An id outside the pool is never used as an
@@ -219,7 +220,7 @@ struct MqTask {
 // most MQ_SLACK below the column's largest scaled score, -inf if it saw no
 // key), the sum l[cb] = sum 2^(c s - m) over all its keys, and the
 // unnormalised accumulators acc[cb][a][b][i] = sum 2^(c s - m) v for dims
-// 64 a + 16 g + 4 i + b, so that (m, l, acc) is a partition state in the
+// 64 a + 16 b + 4 g + i, so that (m, l, acc) is a partition state in the
 // decode kernels' sense; `bad` is set when the
 // table named a block outside the pool.  All threads of the workgroup must
 // call it.  STREAM marks the K/V copies non-temporal (data read once).
@@ -292,7 +293,7 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
         const int pk = wave_v ? piece - Sh::COPIES / 2 : piece;
         const int row = pk * 4 + lane / 16;   // key row inside the step
         const int slot = lane % 16;           // 16-byte slot in the LDS row
-        const int gran = wave_v ? (slot ^ (((row >> 2) & 1) << 3)) : (slot ^ (row & 15));
+        const int gran = wave_v ? (slot ^ ((row & 7) << 1)) : (slot ^ (row & 15));
         cp_blk[j] = row / BS;
         cp_base[j] = (const char*)(wave_v ? pool.v_cache : pool.k_cache) + ((kvh * BS) + row % BS) * ROWB + gran * 16;
     }
@@ -404,46 +405,51 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
         }
     };
 
-    // acc += V^T P^T for step k: dims 64 a + 4 n + b of keys 16 h + 4 g + i,
-    // one operand per (a, b), used by every column block
+    // acc += V^T P^T for step k.  The operand of dims 16 j .. 16 j + 15 comes
+    // from two transposing LDS reads (ds_read_b64_tr_b16), one per 16-key
+    // half h: in each group of 16 lanes, lane l names the 8 bytes of V row
+    // 16 h + 4 g + l / 4 at dims 16 j + 4 (l % 4) .. + 3, and lane n receives
+    // dim 16 j + n of keys 16 h + 4 g + i, i = 0..3 -- the keys of its
+    // weights phi[4 h + i].  Rows past the data are zeroed (they may hold
+    // anything, and 0 * NaN is NaN).
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int tr_row = 4 * g + (n >> 2);          // row inside a 16-key half
+    const int tr_gran = (n & 3) >> 1;             // granule inside the 32-byte dim block
+    const int tr_off = (n & 1) * 8;               // byte inside the granule
     auto pv = [&](int k, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const int k0 = t.key_begin + k * STEP;
-        const char* vb = stage_of(k) + Sh::HALF;
-#pragma unroll
-        for (int aa = 0; aa < 2; ++aa) {
-            u32x2 w[2][4];
+        const __attribute__((address_space(3))) char* vb =
+            (const __attribute__((address_space(3))) char*)(stage_of(k) + Sh::HALF);
+        uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};  // per half: elements (0, 1) and (2, 3)
+        if constexpr (MASKED) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * h + 4 * g + i;
-                    const int gran = (8 * aa + n / 2) ^ (((row >> 2) & 1) << 3);
-                    w[h][i] = *(const u32x2*)(vb + row * ROWB + gran * 16 + (n & 1) * 8);
-                    if constexpr (MASKED) {
-                        if (k0 + row >= t.kv_len) w[h][i] = u32x2{0u, 0u};  // rows past the data may hold anything
-                    }
+                for (int w = 0; w < 2; ++w) {
+                    const int key = k0 + 16 * h + 4 * g + 2 * w;
+                    keep[h][w] = (key < t.kv_len ? 0xffffu : 0u) | (key + 1 < t.kv_len ? 0xffff0000u : 0u);
                 }
-            // operand element 4 h + i = element b of w[h][i]: pairs of keys
-            // share a 32-bit word
+        }
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                u32x4 op;
-                const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+        for (int j = 0; j < 8; ++j) {
+            u32x4 op;
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h) {
+                const int row = 16 * h + tr_row;
+                const int slot = (2 * j + tr_gran) ^ ((row & 7) << 1);
+                const v4i16 e = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(vb + row * ROWB + slot * 16 + tr_off));
+                const u32x2 d = __builtin_bit_cast(u32x2, e);
+                op[2 * h] = d[0] & keep[h][0];
+                op[2 * h + 1] = d[1] & keep[h][1];
+            }
+            const vec A = __builtin_bit_cast(vec, op);
 #pragma unroll
-                    for (int ip = 0; ip < 2; ++ip) {
-                        const uint32_t lo = w[h][2 * ip][b >> 1];
-                        const uint32_t hi = w[h][2 * ip + 1][b >> 1];
-                        op[2 * h + ip] = __builtin_amdgcn_perm(hi, lo, sel);
-                    }
-                const vec A = __builtin_bit_cast(vec, op);
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    acc[cb][aa][b] = Ops::mma(A, phi[cb], acc[cb][aa][b]);
-                    acc[cb][aa][b] = Ops::mma(A, plo[cb], acc[cb][aa][b]);
-                }
+            for (int cb = 0; cb < CB; ++cb) {
+                acc[cb][j >> 2][j & 3] = Ops::mma(A, phi[cb], acc[cb][j >> 2][j & 3]);
+                acc[cb][j >> 2][j & 3] = Ops::mma(A, plo[cb], acc[cb][j >> 2][j & 3]);
             }
         }
     };

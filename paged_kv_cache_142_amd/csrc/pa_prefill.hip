@@ -170,8 +170,8 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     bool bad;
     mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM>(a.pool, t, smem, m, l, acc, bad);
 
-    // ---- output: column n of each block, dims 64 a + 16 g + 4 i + b, four
-    // consecutive dims (b = 0..3) per store
+    // ---- output: column n of each block, dims 64 a + 16 b + 4 g + i, four
+    // consecutive dims (i = 0..3) per store
 #pragma unroll
     for (int cb = 0; cb < PREFILL_CB; ++cb) {
         if (!t.cvalid[cb]) continue;
@@ -180,9 +180,8 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                store_out4(a.out, a.out_dtype, base + 64 * aa + 16 * g + 4 * i,
-                           f32x4{acc[cb][aa][0][i], acc[cb][aa][1][i], acc[cb][aa][2][i], acc[cb][aa][3][i]} * inv);
+            for (int b = 0; b < 4; ++b)
+                store_out4(a.out, a.out_dtype, base + 64 * aa + 16 * b + 4 * g, acc[cb][aa][b] * inv);
     }
 }
 

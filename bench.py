@@ -38,6 +38,9 @@ KERNEL_SOURCES = ["paged_kv_cache_142_amd/csrc/pa_decode_kernel.hpp", "paged_kv_
                   "paged_kv_cache_142_amd/csrc/pa_common.hpp", "paged_kv_cache_142_amd/csrc/pa_decode_bf16.hip",
                   "paged_kv_cache_142_amd/csrc/pa_decode_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partition_gqa_traffic.json")
+# shared_prefix_long: 8 prompts of this many tokens, 6 beams each; the prompts'
+# K/V (268 MB, twice with two pool copies) exceed the 256 MB Infinity Cache
+LONG_PROMPT = 8192
 
 
 def _parse():
@@ -47,7 +50,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="gqa",
                    choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow",
-                            "shared_prefix_grouped", "shared_prefix_cow_grouped", "prefill", "prefill_chunk"])
+                            "shared_prefix_grouped", "shared_prefix_cow_grouped", "shared_prefix_long",
+                            "shared_prefix_long_grouped", "prefill", "prefill_chunk"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=512)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -263,6 +267,8 @@ def _workload(name, seed, partition_size):
     import workloads
     if name.startswith("shared_prefix_cow"):
         return shared_prefix_step(seed, partition_size, 1032)
+    if name.startswith("shared_prefix_long"):
+        return shared_prefix_step(seed, partition_size, LONG_PROMPT)
     if name.startswith("shared_prefix"):
         return shared_prefix_step(seed, partition_size, 1024)
     if name == "gqa":
@@ -505,7 +511,8 @@ def main():
     if args.config.endswith("_grouped"):  # 8 prompts x 6 beams, consecutive; the prompt's whole blocks are shared
         beams = 6
         starts = np.arange(0, wl.num_seqs + 1, beams, dtype=np.int32)
-        prompt_len = 1032 if args.config.startswith("shared_prefix_cow") else 1024
+        prompt_len = (1032 if args.config.startswith("shared_prefix_cow") else
+                      LONG_PROMPT if args.config.startswith("shared_prefix_long") else 1024)
         shared = prompt_len // wl.block_size * wl.block_size
         groups = (starts, np.full(len(starts) - 1, shared, np.int32))
     dev = Device(wl, pools=args.pools, groups=groups)
@@ -605,8 +612,11 @@ def main():
     }
     if wl.name.startswith("shared_prefix"):
         line["config"]["unique_kv_bytes_per_step"] = unique_kv_bytes(wl)
-        line["config"]["cache_assisted"] = ("prompt blocks are shared by 6 beams: the logical KV bytes are read "
-                                            "from far fewer distinct bytes, which fit in the Infinity Cache")
+        distinct = unique_kv_bytes(wl) * args.pools
+        line["config"]["cache_assisted"] = (
+            "prompt blocks are shared by 6 beams: the logical KV bytes are read from far fewer distinct bytes"
+            + (", which fit in the 256 MB Infinity Cache" if distinct < 256e6 else
+               f" ({distinct / 1e6:.0f} MB over the pool copies, more than the 256 MB Infinity Cache)"))
         line["unique_kv_GBs"] = round(unique_kv_bytes(wl) / (ms_per_step * 1e-3) / 1e9, 2)
         if groups is not None:
             line["config"]["decode"] = ("pa_decode_shared_prefix: groups of 6 beams, the prompt's whole blocks "

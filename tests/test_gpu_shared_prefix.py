@@ -27,7 +27,8 @@ def _assemble(wl, seed):
     """Block manager + device pool after prompt fill, fork, CoW and suffix writes."""
     B, Hkv, d = wl.block_size, wl.num_kv_heads, wl.head_dim
     prompt_blocks = -(-wl.prompt_len // B)
-    pool = wl.num_prompts * prompt_blocks + wl.num_seqs * (-(-256 // B) + 2) + 8
+    longest_suffix = max(256, int(wl.suffix_lens.max()))
+    pool = wl.num_prompts * prompt_blocks + wl.num_seqs * (-(-longest_suffix // B) + 2) + 8
     bm = pa.BlockManager(pool, B, free_order=np.random.default_rng(seed).permutation(pool))
     shape = (pool, Hkv, B, d)
     kc, vc = poison_device(shape, "bf16"), poison_device(shape, "bf16")
@@ -303,3 +304,27 @@ def test_shared_prefix_decode_regrouped_workspace():
     case2 = (lens, tables, np.arange(N + 1, dtype=np.int32), np.zeros(N, np.int32), hk, hv, q)
     _run_grouped(case2, fmt="bf16", block_size=16, partition_size=P, max_prefix_len=3 * P, check_plain=False,
                  ws=ws)
+
+
+def test_shared_prefix_decode_long_prompt():
+    """Two 4096-token prompts forked into 4 beams each: eight shared
+    partitions per group, computed once, then merged with each beam's own."""
+    wl = workloads.shared_prefix(4, prompt_len=4096, num_prompts=2, beams=4, max_suffix=600)
+    print("[case] shared_prefix_decode prompt=4096 prompts=2 beams=4", flush=True)
+    bm, beams, kc, vc, hk, hv, tables, pairs = _assemble(wl, 4)
+    lens = wl.seq_lens()
+    msl = int(lens.max())
+    starts, prefix, shared = _beam_groups(wl)
+    q = to_device(wl.q, "bf16")
+    t_dev, l_dev = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    ws = torch.empty(pa.pa_decode_workspace_size(wl.num_seqs, wl.num_heads, wl.head_dim, msl, 512),
+                     dtype=torch.uint8, device="cuda")
+    out = poison_device((wl.num_seqs, wl.num_heads, wl.head_dim), "f32")
+    pa.pa_decode_shared_prefix(out, q, kc, vc, t_dev, l_dev, msl, float(wl.scale), 512, ws,
+                               group_start=starts, group_prefix=prefix, max_group_size=wl.beams,
+                               max_prefix_len=shared)
+    torch.cuda.synchronize()
+    expect = oracle.paged_decode(wl.q, "bf16", hk, hv, "bf16", tables, lens, wl.block_size, float(wl.scale))
+    got = out_as_f64(out)
+    assert_close(got, expect, TOL["bf16"], "shared-prefix decode, 4096-token prompts")
+    assert_close(got[wl.extreme], expect[wl.extreme], TOL["bf16"], "extreme-logit half")

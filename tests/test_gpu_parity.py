@@ -185,8 +185,9 @@ def _sample_rows(wl, k, seed=0):
     return sorted(rows)
 
 
-def test_gqa_full_size_all_rows():
-    _run_and_check(workloads.gqa(0))
+@pytest.mark.parametrize("partition_size", [768, 512])
+def test_gqa_full_size_all_rows(partition_size):
+    _run_and_check(workloads.gqa(0, partition_size=partition_size))
 
 
 def test_mha_full_size_sampled():

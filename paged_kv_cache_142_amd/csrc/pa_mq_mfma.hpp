@@ -253,8 +253,6 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
             const u32x4 v = t.cvalid[cb] ? (qp[c] ^ qsign) : u32x4{0, 0, 0, 0};
             qop[cb][c] = __builtin_bit_cast(vec, v);
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[cb][c]));  // resident before the copies start
     }
 
     // ---- block ids of the key range into LDS, in windows of ID_CAP
@@ -276,7 +274,12 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     if (threadIdx.x == 0) *bad_flag = 0;
     __syncthreads();
     int window = 0;  // first block (relative to blk0) held in `ids`
-    load_ids(0);
+    load_ids(0);  // in flight together with the query loads above
+    // the queries are resident before the copies start (their waits count copies only)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[cb][c]));
     __syncthreads();
 
     // ---- copies of one step: wave w copies CPW 1 KiB pieces (waves 0 .. W/2-1

@@ -52,29 +52,38 @@ struct PrefillArgs {
     int tiles;  // upper bound of the query tiles of one sequence
 };
 
-// Tiles of sequence i (0 past the last sequence or for rows that cannot be
+// A sequence's query range and length, as one lane loads them.
+struct PrefillSeq {
+    int q0, q1, T;
+};
+
+// Tiles of the sequence whose range `r` holds (0 for rows that cannot be
 // addressed).
 template <int TQ>
-__device__ __forceinline__ int prefill_tiles_of(const PrefillArgs& a, int i) {
-    if (i >= a.num_seqs) return 0;
-    const int q0 = a.query_start[i];
-    const int q1 = a.query_start[i + 1];
-    if (q0 < 0 || q1 < q0 || q1 > a.total_q) return 0;
-    return (q1 - q0 + TQ - 1) / TQ;
+__device__ __forceinline__ int prefill_tiles(const PrefillArgs& a, const PrefillSeq& r) {
+    if (r.q0 < 0 || r.q1 < r.q0 || r.q1 > a.total_q) return 0;
+    return (r.q1 - r.q0 + TQ - 1) / TQ;
+}
+
+__device__ __forceinline__ PrefillSeq prefill_seq(const PrefillArgs& a, int i) {
+    if (i >= a.num_seqs) return PrefillSeq{0, 0, 0};
+    return PrefillSeq{a.query_start[i], a.query_start[i + 1], a.seq_lens[i]};
 }
 
 // The p-th tile of the order "highest tile index first, then sequence
 // index", computed by one wavefront (sequences spread over the lanes in
 // chunks of 64).  With c(j) = sum_i max(tiles_i - j, 0), the items of tile
 // index j are c(j+1) .. c(j) - 1: a binary search on j, then the r-th
-// sequence (in index order) that has more than j tiles.
+// sequence (in index order) that has more than j tiles.  The sequence's
+// query range and length come back with it (loaded with the counts).
 template <int TQ>
-__device__ bool prefill_item(const PrefillArgs& a, int p, int& seq, int& tile) {
+__device__ bool prefill_item(const PrefillArgs& a, int p, int& seq, int& tile, PrefillSeq& sr) {
     const int lane = threadIdx.x & 63;
-    const int t0 = prefill_tiles_of<TQ>(a, lane);  // the first chunk stays in a register
-    auto count_from = [&](int j) {                  // c(j), uniform
+    const PrefillSeq r0 = prefill_seq(a, lane);  // the first chunk stays in registers
+    const int t0 = prefill_tiles<TQ>(a, r0);
+    auto count_from = [&](int j) {  // c(j), uniform
         int x = max(t0 - j, 0);
-        for (int c = 64; c < a.num_seqs; c += 64) x += max(prefill_tiles_of<TQ>(a, c + lane) - j, 0);
+        for (int c = 64; c < a.num_seqs; c += 64) x += max(prefill_tiles<TQ>(a, prefill_seq(a, c + lane)) - j, 0);
         return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63);
     };
     if (p >= count_from(0)) return false;
@@ -88,22 +97,26 @@ __device__ bool prefill_item(const PrefillArgs& a, int p, int& seq, int& tile) {
     }
     int r = p - count_from(lo + 1);
     for (int c = 0; c < a.num_seqs; c += 64) {
-        const bool has = (c == 0 ? t0 : prefill_tiles_of<TQ>(a, c + lane)) > lo;
+        const PrefillSeq rc = c == 0 ? r0 : prefill_seq(a, c + lane);
+        const bool has = prefill_tiles<TQ>(a, rc) > lo;
         const uint64_t m = __builtin_amdgcn_ballot_w64(has);
         const int cnt = __builtin_popcountll(m);
         if (r < cnt) {
             const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
             const uint64_t hit = __builtin_amdgcn_ballot_w64(has && below == r);
             if (hit == 0) return false;  // cannot happen for r < cnt
-            seq = c + __builtin_ctzll(hit);
+            const int l = __builtin_ctzll(hit);
+            seq = c + l;
             tile = lo;
+            sr.q0 = __builtin_amdgcn_readlane(rc.q0, l);
+            sr.q1 = __builtin_amdgcn_readlane(rc.q1, l);
+            sr.T = __builtin_amdgcn_readlane(rc.T, l);
             return true;
         }
         r -= cnt;
     }
     return false;
 }
-
 
 template <Fmt KV, int D, int BS, int G>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs a) {
@@ -119,12 +132,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     const int H = a.pool.num_kv_heads;
     const int kvh = (int)(blockIdx.x % H);
     int seq, tile;
-    if (!prefill_item<Sh::TQ>(a, (int)(blockIdx.x / H), seq, tile)) return;
-
-    const int q0 = a.query_start[seq];
-    const int q1 = a.query_start[seq + 1];
-    const int T = a.seq_lens[seq];
-    if (q0 < 0 || q1 < q0 || q1 > a.total_q) return;  // rows that cannot be addressed
+    PrefillSeq sr;
+    if (!prefill_item<Sh::TQ>(a, (int)(blockIdx.x / H), seq, tile, sr)) return;
+    const int q0 = sr.q0, q1 = sr.q1, T = sr.T;  // the range can be addressed: the sequence has tiles
     const int Q = q1 - q0;
     const int tok_lo = tile * Sh::TQ;
     if (tok_lo >= Q) return;

@@ -221,9 +221,9 @@ struct MqTask {
 // key), the sum l[cb] = sum 2^(c s - m) over all its keys, and the
 // unnormalised accumulators acc[cb][a][b][i] = sum 2^(c s - m) v for dims
 // 64 a + 16 b + 4 g + i, so that (m, l, acc) is a partition state in the
-// decode kernels' sense; `bad` is set when the
-// table named a block outside the pool.  All threads of the workgroup must
-// call it.  STREAM marks the K/V copies non-temporal (data read once).
+// decode kernels' sense; `bad` is set when the table named a block outside
+// the pool.  All threads of the workgroup must call it.  STREAM marks the
+// K/V copies non-temporal (data read once).
 template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM>
 __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, float (&m)[CB], float (&l)[CB],
                         f32x4 (&acc)[CB][2][4], bool& bad) {

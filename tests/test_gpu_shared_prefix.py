@@ -122,7 +122,7 @@ def _beam_groups(wl):
     return starts, prefix, shared
 
 
-@pytest.mark.parametrize("prompt_len,partition_size", [(1032, 512), (1024, 512), (1032, 256), (1024, 1024)])
+@pytest.mark.parametrize("prompt_len,partition_size", [(1032, 512), (1024, 512), (1032, 256), (1024, 256), (1024, 1024)])
 def test_shared_prefix_decode_beams(prompt_len, partition_size):
     """pa_decode_shared_prefix over the forked beams: the oracle's plain
     attention over each beam's logical rows, and pa_decode's output."""

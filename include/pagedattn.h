@@ -32,6 +32,20 @@
  *   device-supplied index that would address memory: an out-of-range slot or
  *   block pair is skipped, and a sequence whose length or block ids are out
  *   of range gets a row of NaN in `out` instead of a memory access.
+ * - The checked build (libpagedattn_checked.so, compiled with
+ *   PA_CHECK_CONTENTS=1; same ABI) copies the index arrays each call reads
+ *   to the host before launching, synchronising `stream`, and returns
+ *   PA_ERR_CONTENT without launching anything when they break a contract
+ *   stated below: a slot past the pool or used twice in one call; a copy or
+ *   swap pair outside its pools, a destination named twice, or (copy) a
+ *   destination that is also a source; a length outside [0, max_seq_len] or
+ *   needing more than max_blocks_per_seq blocks; a table entry a sequence
+ *   reads that is outside the pool; group_start or query_start not
+ *   non-decreasing over their stated range; a negative prefix or a member
+ *   whose table differs from its group's first sequence's over the shared
+ *   tokens; a query count above max_query_len or above the sequence's
+ *   length.  It is a debugging aid: its calls synchronise and cannot be
+ *   captured in a graph.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -64,7 +78,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = -4, /* valid but not built: head_dim, block_size, GQA group */
     PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_size()   */
     PA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch           */
-    PA_ERR_MEMORY = -7       /* a pool the GPU cannot address (pa_swap_blocks)      */
+    PA_ERR_MEMORY = -7,      /* a pool the GPU cannot address (pa_swap_blocks)      */
+    PA_ERR_CONTENT = -8      /* checked build only: device contents break the contract */
 } pa_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */

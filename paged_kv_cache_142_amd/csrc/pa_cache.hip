@@ -146,6 +146,7 @@ extern "C" const char* pa_status_string(int status) {
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
         case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
         case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pool is neither device memory nor pinned host memory the device can address";
+        case PA_ERR_CONTENT: return "PA_ERR_CONTENT: device contents break the call's contract (checked build)";
         default: return "unknown pa_status";
     }
 }
@@ -165,6 +166,10 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
     const int64_t total = (int64_t)num_tokens * 2 * num_kv_heads * granules_per_row;
     const int64_t grid = (total + 255) / 256;
     if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+#if PA_CHECK_CONTENTS
+    const int checked = check::slots(slot_mapping, num_tokens, num_blocks, block_size, (hipStream_t)stream);
+    if (checked != PA_OK) return checked;
+#endif
     hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0,
                        (hipStream_t)stream, (const u32x4*)key, (const u32x4*)value,
                        (u32x4*)k_cache, (u32x4*)v_cache, slot_mapping, total, granules_per_row,
@@ -191,6 +196,10 @@ extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, int 
     if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
     const int64_t slots = (int64_t)num_blocks * block_size;
     const hipStream_t s = (hipStream_t)stream;
+#if PA_CHECK_CONTENTS
+    const int checked = check::slots(slot_mapping, num_tokens, num_blocks, block_size, s);
+    if (checked != PA_OK) return checked;
+#endif
 #define PA_LAUNCH_Q(F)                                                                          \
     hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<F>, dim3((unsigned)grid), dim3(256), 0, s, \
                        (const char*)key, (const char*)value, (uint8_t*)k_cache, (uint8_t*)v_cache,  \
@@ -207,9 +216,11 @@ extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, int 
 }
 
 namespace pa {
+// same_pool: a copy inside one pool (pa_copy_blocks) rather than between two (pa_swap_blocks)
 static int launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
                               const int64_t* block_pairs, int num_pairs, int num_kv_heads, int head_dim,
-                              int block_size, int src_blocks, int dst_blocks, int kv_dtype, void* stream) {
+                              int block_size, int src_blocks, int dst_blocks, int kv_dtype, bool same_pool,
+                              void* stream) {
     if (!valid_kv_dtype(kv_dtype)) return PA_ERR_DTYPE;
     if (num_pairs < 0 || num_kv_heads <= 0 || src_blocks <= 0 || dst_blocks <= 0 || head_dim <= 0 ||
         block_size <= 0)
@@ -222,6 +233,12 @@ static int launch_copy_blocks(const void* src_k, const void* src_v, void* dst_k,
     const int64_t granules = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype) / 16;
     if (granules > 0x7fffffffLL) return PA_ERR_SHAPE;
     const unsigned gx = (unsigned)((granules + 255) / 256);
+#if PA_CHECK_CONTENTS
+    const int checked = check::pairs(block_pairs, num_pairs, src_blocks, dst_blocks, same_pool, (hipStream_t)stream);
+    if (checked != PA_OK) return checked;
+#else
+    (void)same_pool;
+#endif
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, (unsigned)num_pairs, 2), dim3(256), 0,
                        (hipStream_t)stream, (const u32x4*)src_k, (const u32x4*)src_v, (u32x4*)dst_k,
                        (u32x4*)dst_v, block_pairs, (int)granules, (int64_t)src_blocks, (int64_t)dst_blocks);
@@ -233,7 +250,7 @@ extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block
                               int num_pairs, int num_kv_heads, int head_dim, int block_size,
                               int num_blocks, int kv_dtype, void* stream) {
     return pa::launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, num_kv_heads,
-                                  head_dim, block_size, num_blocks, num_blocks, kv_dtype, stream);
+                                  head_dim, block_size, num_blocks, num_blocks, kv_dtype, true, stream);
 }
 
 namespace pa {
@@ -265,5 +282,5 @@ extern "C" int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k,
             if (!pa::device_addressable(p)) return PA_ERR_MEMORY;
     }
     return pa::launch_copy_blocks(src_k, src_v, dst_k, dst_v, block_pairs, num_pairs, num_kv_heads, head_dim,
-                                  block_size, src_num_blocks, dst_num_blocks, kv_dtype, stream);
+                                  block_size, src_num_blocks, dst_num_blocks, kv_dtype, false, stream);
 }

@@ -10,6 +10,13 @@
 
 #include "pagedattn.h"
 
+#ifndef PA_CHECK_CONTENTS
+#define PA_CHECK_CONTENTS 0
+#endif
+#if PA_CHECK_CONTENTS
+#include "pa_checks.hpp"
+#endif
+
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

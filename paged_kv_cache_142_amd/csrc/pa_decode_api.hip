@@ -352,10 +352,24 @@ extern "C" size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head
                                    pa::num_partitions(max_seq_len, partition_size));
 }
 
+#if PA_CHECK_CONTENTS
+#define PA_CHECK_SEQUENCES()                                                                               \
+    do {                                                                                                   \
+        const int checked = pa::check::sequences(seq_lens, block_tables, num_seqs, max_blocks_per_seq,     \
+                                                 max_seq_len, block_size, num_blocks, (hipStream_t)stream); \
+        if (checked != PA_OK) return checked;                                                              \
+    } while (0)
+#else
+#define PA_CHECK_SEQUENCES() \
+    do {                     \
+    } while (0)
+#endif
+
 extern "C" int pa_decode_partition(PA_DECODE_PARAMS) {
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
     if (st != PA_OK || pr.nothing_to_do) return st;
+    PA_CHECK_SEQUENCES();
     return pa::run_partition(pr, (hipStream_t)stream);
 }
 
@@ -363,6 +377,7 @@ extern "C" int pa_decode_reduce(PA_DECODE_PARAMS) {
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
     if (st != PA_OK || pr.nothing_to_do) return st;
+    PA_CHECK_SEQUENCES();
     return pa::run_reduce(pr, (hipStream_t)stream);
 }
 
@@ -370,6 +385,7 @@ extern "C" int pa_decode(PA_DECODE_PARAMS) {
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
     if (st != PA_OK || pr.nothing_to_do) return st;
+    PA_CHECK_SEQUENCES();
     const int s1 = pa::run_partition(pr, (hipStream_t)stream);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, (hipStream_t)stream);
@@ -383,6 +399,17 @@ extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_st
     if (num_groups < 0 || max_group_size < 0 || max_prefix_len < 0) return PA_ERR_SHAPE;
     if (num_groups > 0 && (!group_start || !group_prefix)) return PA_ERR_NULL;
     const hipStream_t s = (hipStream_t)stream;
+#if PA_CHECK_CONTENTS
+    {
+        std::vector<int32_t> lens, tables;
+        int checked = pa::check::sequences(seq_lens, block_tables, num_seqs, max_blocks_per_seq, max_seq_len,
+                                           block_size, num_blocks, lens, tables, s);
+        if (checked == PA_OK && num_groups > 0)
+            checked = pa::check::groups(group_start, group_prefix, num_groups, num_seqs, max_blocks_per_seq,
+                                        block_size, lens, tables, s);
+        if (checked != PA_OK) return checked;
+    }
+#endif
     // nothing to share, or a shape the matrix-core tile does not cover: plain decode
     if (num_groups == 0 || max_prefix_len < partition_size || max_group_size == 0 || ((uintptr_t)out & 15u) ||
         !pa::prefix_states_supported(pr.kv_dtype, pr.q_dtype, pr.head_dim, block_size, pr.group)) {

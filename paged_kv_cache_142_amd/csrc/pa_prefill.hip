@@ -252,6 +252,16 @@ extern "C" int pa_prefill(void* out, int out_dtype, const void* q, int q_dtype, 
     if ((((uintptr_t)out) | ((uintptr_t)q) | ((uintptr_t)k_cache) | ((uintptr_t)v_cache)) & 15u) return PA_ERR_SHAPE;
     const long long items_max = (total_q + 7) / 8 + (long long)num_seqs;  // the smallest tile is 8 tokens
     if (items_max * num_kv_heads > 0x7fffffffLL) return PA_ERR_SHAPE;
+#if PA_CHECK_CONTENTS
+    {
+        std::vector<int32_t> lens, tables;
+        int checked = check::sequences(seq_lens, block_tables, num_seqs, max_blocks_per_seq, max_seq_len, block_size,
+                                       num_blocks, lens, tables, (hipStream_t)stream);
+        if (checked == PA_OK)
+            checked = check::queries(query_start, num_seqs, total_q, max_query_len, lens, (hipStream_t)stream);
+        if (checked != PA_OK) return checked;
+    }
+#endif
     PrefillArgs a;
     a.out = out;
     a.out_dtype = out_dtype;

@@ -1,0 +1,228 @@
+"""The checked build (``libpagedattn_checked.so``) on the GPU: with valid
+device contents it gives bitwise the release build's results; each contract
+violation in device contents returns PA_ERR_CONTENT before anything runs, so
+outputs and pools stay as they were.
+
+The binding's calls go to whichever library ``PAGEDATTN_LIBRARY`` names, so
+each test switches it for the duration of the test."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_142_amd as pa
+import workloads
+from gpu_util import DeviceCase, poison_device, to_device
+from paged_kv_cache_142_amd import _lib
+from test_gpu_prefill import PrefillCase
+from test_gpu_shared_prefix import _grouped_case
+
+pytestmark = pytest.mark.gpu
+
+CONTENT = -8
+
+
+@pytest.fixture
+def checked(monkeypatch):
+    monkeypatch.setenv("PAGEDATTN_LIBRARY", _lib.CHECKED_LIB_PATH)
+
+
+def _rejects(call, what):
+    with pytest.raises(pa.PagedAttnError) as e:
+        call()
+    assert e.value.status == CONTENT, (what, e.value.status)
+    print(f"[checked] {what}: PA_ERR_CONTENT", flush=True)
+
+
+def _bytes(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def _release_and_checked(monkeypatch, run):
+    """run() on a fresh case with each library; returns both results."""
+    monkeypatch.delenv("PAGEDATTN_LIBRARY", raising=False)
+    a = run()
+    monkeypatch.setenv("PAGEDATTN_LIBRARY", _lib.CHECKED_LIB_PATH)
+    b = run()
+    return a, b
+
+
+def test_valid_contents_match_release_bitwise(monkeypatch):
+    print("[case] checked build, valid gqa / fp8 / prefill / shared-prefix calls", flush=True)
+
+    def decode_step(wl):
+        def run():
+            case = DeviceCase(wl)
+            case.run_step()
+            torch.cuda.synchronize()
+            return [_bytes(case.out), _bytes(case.k_cache), _bytes(case.v_cache)]
+        return run
+
+    for wl in (workloads.gqa(7, num_seqs=9, max_len=900, partition_size=256),
+               workloads.long_fp8(7, num_seqs=2, seq_len=700, partition_size=256)):
+        a, b = _release_and_checked(monkeypatch, decode_step(wl))
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), wl.name
+
+    pwl = workloads.prefill(7, num_seqs=4, max_len=300, chunk=50, kv_dtype="bf16")
+
+    def prefill():
+        case = PrefillCase(pwl)
+        case.run()
+        return [_bytes(case.out)]
+
+    a, b = _release_and_checked(monkeypatch, prefill)
+    assert np.array_equal(a[0], b[0])
+
+    P = 256
+    groups = [(2 * P, [2 * P + 5, 2 * P + 90, 2 * P]), (P + 16, [P + 16, P + 100])]
+    lens, tables, starts, prefixes, hk, hv, q = _grouped_case(9, num_heads=32, num_kv_heads=8, head_dim=128,
+                                                              block_size=16, fmt="bf16", groups=groups)
+
+    def shared():
+        out = poison_device(q.shape, "f32")
+        msl = int(lens.max())
+        ws = torch.empty(pa.pa_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], msl, P), dtype=torch.uint8,
+                         device="cuda")
+        pa.pa_decode_shared_prefix(out, to_device(q, "bf16"), to_device(hk, "bf16"), to_device(hv, "bf16"),
+                                   torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), msl, 0.088, P, ws,
+                                   group_start=torch.from_numpy(starts).cuda(),
+                                   group_prefix=torch.from_numpy(prefixes).cuda(), max_group_size=3,
+                                   max_prefix_len=int(prefixes.max()))
+        return [_bytes(out)]
+
+    a, b = _release_and_checked(monkeypatch, shared)
+    assert np.array_equal(a[0], b[0])
+
+
+def test_cache_op_violations(checked):
+    wl = workloads.gqa(8, num_seqs=4, max_len=300, partition_size=256)
+    print(f"[case] checked build, cache operations on {wl.num_blocks} blocks", flush=True)
+    case = DeviceCase(wl)
+    torch.cuda.synchronize()
+    k0, v0 = _bytes(case.k_cache), _bytes(case.v_cache)
+    keys, values = case.step_keys, case.step_values
+    B = wl.block_size
+    s = case.step_slots.clone()
+    dup = s.clone()
+    dup[1] = dup[0]
+    _rejects(lambda: pa.pa_reshape_and_cache(keys, values, case.k_cache, case.v_cache, dup), "duplicate slot")
+    past = s.clone()
+    past[2] = wl.num_blocks * B
+    _rejects(lambda: pa.pa_reshape_and_cache(keys, values, case.k_cache, case.v_cache, past), "slot past the pool")
+    used = wl.block_tables[wl.block_tables >= 0]
+    spare = np.setdiff1d(np.arange(wl.num_blocks), used)
+    pairs = lambda p: torch.tensor(np.array(p, np.int64).reshape(-1, 2), device="cuda")
+    _rejects(lambda: pa.pa_copy_blocks(case.k_cache, case.v_cache, pairs([[used[0], spare[0]], [spare[0], spare[1]]])),
+             "copy destination that is also a source")
+    _rejects(lambda: pa.pa_copy_blocks(case.k_cache, case.v_cache, pairs([[used[0], spare[0]], [used[1], spare[0]]])),
+             "copy destination named twice")
+    _rejects(lambda: pa.pa_copy_blocks(case.k_cache, case.v_cache, pairs([[used[0], wl.num_blocks]])),
+             "copy destination past the pool")
+    host = torch.empty((4,) + tuple(case.k_cache.shape[1:]), dtype=case.k_cache.dtype, pin_memory=True)
+    host_v = torch.empty_like(host, pin_memory=True)
+    _rejects(lambda: pa.pa_swap_blocks(case.k_cache, case.v_cache, host, host_v, pairs([[used[0], 1], [used[1], 1]])),
+             "swap destination named twice")
+    _rejects(lambda: pa.pa_swap_blocks(case.k_cache, case.v_cache, host, host_v, pairs([[used[0], 4]])),
+             "swap destination past the host pool")
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(case.k_cache), k0) and np.array_equal(_bytes(case.v_cache), v0)
+    # negative slots are skipped, not an error
+    neg = s.clone()
+    neg[0] = -1
+    pa.pa_reshape_and_cache(keys, values, case.k_cache, case.v_cache, neg)
+    torch.cuda.synchronize()
+
+
+def test_fp8_scatter_violation(checked):
+    wl = workloads.long_fp8(8, num_seqs=2, seq_len=200, partition_size=256)
+    case = DeviceCase(wl)
+    dup = case.step_slots.clone()
+    dup[1] = dup[0]
+    print("[case] checked build, fp8 scatter", flush=True)
+    _rejects(lambda: pa.pa_reshape_and_cache_fp8(case.step_keys, case.step_values, case.k_cache, case.v_cache,
+                                                 case.k_scale, case.v_scale, dup), "duplicate fp8 slot")
+
+
+def test_decode_violations(checked):
+    wl = workloads.gqa(9, num_seqs=5, max_len=600, partition_size=256)
+    print("[case] checked build, decode lengths and tables", flush=True)
+    case = DeviceCase(wl)
+    case.run_cache_ops()
+    torch.cuda.synchronize()
+    lens = case.seq_lens.clone()
+    lens[3] = wl.max_seq_len + 1
+    _rejects(lambda: pa.pa_decode(**{**case.decode_args(), "seq_lens": lens}), "length above max_seq_len")
+    lens[3] = -1
+    _rejects(lambda: pa.pa_decode_partition(**{**case.decode_args(), "seq_lens": lens}), "negative length")
+    _rejects(lambda: pa.pa_decode_reduce(**{**case.decode_args(), "seq_lens": lens}), "negative length (reduce)")
+    bad = wl.block_tables.copy()
+    i = int(np.argmax(wl.seq_lens))
+    bad[i, (int(wl.seq_lens[i]) - 1) // wl.block_size] = wl.num_blocks
+    _rejects(lambda: case.decode(block_tables=torch.from_numpy(bad).cuda()), "table entry past the pool")
+    torch.cuda.synchronize()
+    assert torch.isnan(case.out).all(), "a rejected call wrote the output"
+    # entries a sequence does not read may hold anything
+    ok = wl.block_tables.copy()
+    j = int(np.argmin(wl.seq_lens))
+    nb = -(-int(wl.seq_lens[j]) // wl.block_size)
+    if nb < ok.shape[1]:
+        ok[j, nb:] = 1 << 30
+    case.decode(block_tables=torch.from_numpy(ok).cuda())
+    torch.cuda.synchronize()
+    assert not torch.isnan(case.out).any()
+
+
+def test_shared_prefix_violations(checked):
+    P = 256
+    groups = [(2 * P, [2 * P + 5, 2 * P + 90, 2 * P]), (P + 16, [P + 16, P + 100])]
+    lens, tables, starts, prefixes, hk, hv, q = _grouped_case(10, num_heads=32, num_kv_heads=8, head_dim=128,
+                                                              block_size=16, fmt="bf16", groups=groups)
+    print("[case] checked build, shared-prefix groups", flush=True)
+    kc, vc, qd = to_device(hk, "bf16"), to_device(hv, "bf16"), to_device(q, "bf16")
+    msl = int(lens.max())
+    ws = torch.empty(pa.pa_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], msl, P), dtype=torch.uint8,
+                     device="cuda")
+    out = poison_device(q.shape, "f32")
+
+    def call(t=tables, st=starts, pr=prefixes):
+        pa.pa_decode_shared_prefix(out, qd, kc, vc, torch.from_numpy(t).cuda(), torch.from_numpy(lens).cuda(), msl,
+                                   0.088, P, ws, group_start=torch.from_numpy(st).cuda(),
+                                   group_prefix=torch.from_numpy(pr).cuda(), max_group_size=3, max_prefix_len=2 * P)
+
+    diverged = tables.copy()
+    diverged[1, 5] = diverged[0, 5] + 1 if diverged[0, 5] + 1 < hk.shape[0] else diverged[0, 5] - 1
+    _rejects(lambda: call(t=diverged), "member table differs inside the shared prefix")
+    _rejects(lambda: call(st=np.array([0, 3, 4], np.int32)), "group_start not ending at num_seqs")
+    _rejects(lambda: call(st=np.array([0, 6, 5], np.int32)), "group_start decreasing")
+    _rejects(lambda: call(pr=np.array([2 * P, -1], np.int32)), "negative prefix")
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all(), "a rejected call wrote the output"
+    # past the shared prefix, members' tables may differ
+    after = tables.copy()
+    k = 2 * P // 16
+    after[0, k], after[1, k] = after[1, k], after[0, k]
+    assert lens[0] > 2 * P and lens[1] > 2 * P
+    call(t=after)
+    call()
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+
+
+def test_prefill_violations(checked):
+    wl = workloads.prefill(11, num_seqs=3, max_len=200, chunk=30, kv_dtype="bf16")
+    print("[case] checked build, prefill query counts", flush=True)
+    case = PrefillCase(wl)
+    qs = wl.query_start.copy()
+    bad_end = qs.copy()
+    bad_end[-1] -= 1
+    _rejects(lambda: case.run(query_start=torch.from_numpy(bad_end).cuda()), "query_start not ending at total_q")
+    qmax = int(wl.query_lens.max())
+    _rejects(lambda: case.run(max_query_len=qmax - 1), "query count above max_query_len")
+    lens = wl.cache.seq_lens.copy()
+    i = int(np.argmax(wl.query_lens))
+    lens[i] = wl.query_lens[i] - 1
+    _rejects(lambda: case.run(seq_lens=torch.from_numpy(lens).cuda()), "query count above the sequence length")
+    assert torch.isnan(case.out).all(), "a rejected call wrote the output"
+    case.run()
+    assert not torch.isnan(case.out).any()

@@ -185,20 +185,21 @@ def _sample_rows(wl, k, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("partition_size", [768, 512])
-def test_gqa_full_size_all_rows(partition_size):
-    _run_and_check(workloads.gqa(0, partition_size=partition_size))
+@pytest.mark.parametrize("seed,partition_size", [(0, 768), (0, 512), (1, 768), (2, 768)])
+def test_gqa_full_size_all_rows(seed, partition_size):
+    _run_and_check(workloads.gqa(seed, partition_size=partition_size))
 
 
-def test_mha_full_size_sampled():
-    wl = workloads.mha(0)
-    _run_and_check(wl, rows=_sample_rows(wl, 24))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mha_full_size_sampled(seed):
+    wl = workloads.mha(seed)
+    _run_and_check(wl, rows=_sample_rows(wl, 24, seed))
 
 
-@pytest.mark.parametrize("block_size", [16, 32])
-def test_long_fp8_full_size_sampled(block_size):
-    wl = workloads.long_fp8(0, block_size=block_size)
-    _run_and_check(wl, rows=[0, 7, 15])
+@pytest.mark.parametrize("seed,block_size", [(0, 16), (0, 32), (1, 16), (2, 32)])
+def test_long_fp8_full_size_sampled(seed, block_size):
+    wl = workloads.long_fp8(seed, block_size=block_size)
+    _run_and_check(wl, rows=[0, 7, 15] if seed == 0 else sorted({0, 15, 3 + 4 * seed}))
 
 
 def test_empty_and_invalid_rows():

@@ -1,17 +1,24 @@
 """Benchmark of one decode step of the paged-attention hot path on one GPU.
 
-A step is one pass of the whole path over the batch: scatter of each
-sequence's new token into the pool (``pa_reshape_and_cache``), the step's
-block copies (``pa_copy_blocks``), and the decode itself
-(``pa_decode_partition`` then ``pa_decode_reduce``, i.e. ``pa_decode``).
+A step is one pass of the whole path over the batch: the step's block
+copies (``pa_copy_blocks``), the scatter of each sequence's new token into
+the pool, and the decode itself.  Where one call can do the last two
+(bf16/f16/f32 pools decoded with ``pa_decode``), the step is
+``pa_copy_blocks`` then ``pa_decode_append``, which stores the tokens inside
+the partition kernel for four query heads per kv head; otherwise (FP8 pools
+quantized on write, grouped shared-prefix decode) it is the scatter
+(``pa_reshape_and_cache[_fp8]``), the copies, and the decode
+(``pa_decode_partition`` then ``pa_decode_reduce``, or
+``pa_decode_shared_prefix``).  ``step_calls`` in the output names them.
 Inputs are resident in HBM before the timed region.  Throughput is the
 effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
 By default two copies of the K/V pool alternate between steps, so that no
 step finds the previous step's K/V in the 256 MB Infinity Cache (on MI355X
 this costs about 1% against re-reading one pool; ``--pools 1`` for that).
 Also reported: ``pa_decode`` alone, called back to back (``decode_alone_*``),
-and per-call durations from a second loop with HIP events around each call
-(``kernels_us``), from which the roofline of the partition launch is taken.
+and per-call durations from a second loop with HIP events around each of
+the separate launches (scatter, copies, partition, reduce: ``kernels_us``),
+from which the roofline of the partition launch is taken.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
@@ -47,7 +54,9 @@ def _parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=500,
+                   help="untimed steps first (default 500: with 20 the first timed steps still ran about 5%% "
+                        "slower than the steady state on MI355X)")
     p.add_argument("--config", default="gqa",
                    choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow",
                             "shared_prefix_grouped", "shared_prefix_cow_grouped", "shared_prefix_long",
@@ -370,8 +379,15 @@ class Device:
                                max_group_size=int(np.diff(starts).max()), max_prefix_len=int(prefix.max()))
         self.pools = [(self.k_cache, self.v_cache)] + [(self.k_cache.clone(), self.v_cache.clone())
                                                         for _ in range(pools - 1)]
+        # The timed step stores the new tokens inside the decode call
+        # (pa_decode_append: copy-on-write copies first, then one call) where
+        # that call applies; the per-call timing loop keeps the four separate
+        # launches (scatter, copy, partition, reduce).
+        self.append_fused = (groups is None and not self.quantize_step
+                             and self.step_keys.shape[0] == wl.num_seqs)
         # identical calls every step: marshal the C arguments once per pool copy
-        self.call_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
+        self.call_sets = [self._make_calls(kc, vc, fused=self.append_fused) for kc, vc in self.pools]
+        self.part_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
         self.decode_calls = [self._decode_call(kc, vc) for kc, vc in self.pools]
         self.calls = self.call_sets[0]
         torch.cuda.synchronize()
@@ -382,11 +398,15 @@ class Device:
             return self.pa.prepared("pa_decode_shared_prefix", **dargs, **self.groups)
         return self.pa.prepared("pa_decode", **dargs)
 
-    def _make_calls(self, k_cache=None, v_cache=None):
+    def _make_calls(self, k_cache=None, v_cache=None, fused=False):
         pa, kv = self.pa, self.kv
         kc = self.k_cache if k_cache is None else k_cache
         vc = self.v_cache if v_cache is None else v_cache
         dargs = dict(self.dargs, k_cache=kc, v_cache=vc)
+        if fused:
+            copy = pa.prepared("pa_copy_blocks", kc, vc, self.pairs, kv_dtype=kv) if self.pairs.numel() else (
+                lambda: None)
+            return [copy, pa.prepared("pa_decode_append", **dargs, key=self.step_keys, value=self.step_values)]
         scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, kc, vc,
                                self.k_scale, self.v_scale, self.step_slots)
                    if self.quantize_step else
@@ -411,7 +431,7 @@ class Device:
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                calls = self._make_calls()
+                calls = self._make_calls(fused=self.append_fused)
                 for call in calls:
                     call()
         torch.cuda.current_stream().wait_stream(side)
@@ -419,11 +439,11 @@ class Device:
         return g
 
     def step(self, i=0, ev=None):
-        calls = self.call_sets[i % len(self.call_sets)]
         if ev is None:
-            for call in calls:
+            for call in self.call_sets[i % len(self.call_sets)]:
                 call()
             return
+        calls = self.part_sets[i % len(self.part_sets)]  # separate launches, an event around each
         ev[0].record()
         for k, call in enumerate(calls):
             call()
@@ -611,6 +631,10 @@ def main():
             [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
+        "step_calls": (["pa_copy_blocks", "pa_decode_append"] if dev.append_fused else
+                       ["pa_reshape_and_cache" + ("_fp8" if dev.quantize_step else ""), "pa_copy_blocks",
+                        "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
+                        *([] if groups is not None else ["pa_decode_reduce"])]),
         "pool_copies": args.pools,
         "roofline": {"kernel": roof_kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -282,6 +282,39 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
                      int partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- store each sequence's newest token, then pa_decode.
+ *
+ * A decode step first writes the K and V rows of the token it has just
+ * computed into the cache, then attends over all cached tokens, that token
+ * included (the explainer's section "Attention計算": K holds every token so
+ * far).  This call does both: for every sequence i with T = seq_lens[i] > 0,
+ * it stores key[i] and value[i] (all kv heads) at position T - 1, i.e. in
+ * row (T-1) % block_size of block block_tables[i][(T-1) / block_size], as
+ * pa_reshape_and_cache would with that slot; then it computes exactly what
+ * pa_decode computes.  The result and the pool are bitwise those of
+ * pa_reshape_and_cache followed by pa_decode.
+ *
+ * For the GQA-4 kernel's shapes (bf16 or f16 K/V, four query heads per kv
+ * head) the store happens inside the partition kernel: the workgroup that
+ * owns a sequence's last partition copies the new rows into the pool and
+ * into its staged tile, saving the separate scatter launch.  Other shapes
+ * launch a small copy kernel first.
+ *   key, value   [num_seqs][num_kv_heads][head_dim] in kv_dtype (for FP8
+ *                pools, E4M3 codes), 16-byte aligned, device
+ *   other arguments: as for pa_decode.  The block that holds position T - 1
+ *                must not be shared with another sequence (copy-on-write is
+ *                the caller's, through pa_copy_blocks, before this call).
+ * Sequences with T == 0 or an invalid length store nothing; a block id
+ * outside the pool stores nothing and gives a NaN row, as in pa_decode.
+ */
+int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                     const void* v_cache, int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* seq_lens, int max_seq_len, int num_seqs, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int num_blocks, float scale, const float* k_scale,
+                     const float* v_scale, int partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream, const void* key, const void* value);
+
+/*
  * pa_decode_shared_prefix -- pa_decode for batches whose sequences share
  * prompt blocks (parallel samples and beams forked from one prompt), reading
  * each shared block once per group instead of once per sequence.

@@ -153,6 +153,9 @@ def prepared(name, *args, **kw):
     fn = getattr(lib, name)
     if name in ("pa_decode", "pa_decode_partition", "pa_decode_reduce"):
         argv = _decode_argv(*args, **kw)
+    elif name == "pa_decode_append":
+        key, value = kw.pop("key"), kw.pop("value")
+        argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
     elif name == "pa_decode_shared_prefix":
         gs, gp, mgs, mpl = (kw.pop(k) for k in ("group_start", "group_prefix", "max_group_size", "max_prefix_len"))
         argv = _decode_argv(*args, **kw) + _group_argv(gs, gp, mgs, mpl)
@@ -197,6 +200,25 @@ def pa_decode(*args, **kw):
     ``v_scale``; see ``include/pagedattn.h``.
     """
     _decode_call("pa_decode", *args, **kw)
+
+
+def _append_argv(key, value, args, kw):
+    q = kw["q"] if "q" in kw else args[1]
+    k_cache = kw["k_cache"] if "k_cache" in kw else args[2]
+    want = (q.shape[0], k_cache.shape[1], k_cache.shape[3])
+    if tuple(key.shape) != want or tuple(value.shape) != want:
+        raise ValueError(f"key and value must be [num_seqs, num_kv_heads, head_dim] = {list(want)}")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype:
+        raise ValueError("key and value must be in the pool's element format")
+    return (_ptr(key), _ptr(value))
+
+
+def pa_decode_append(*args, key, value, **kw):
+    """``pa_decode`` that first stores each sequence's newest token
+    (``key``/``value`` ``[num_seqs][num_kv_heads][head_dim]``) at position
+    ``seq_lens - 1``; the other arguments are ``pa_decode``'s."""
+    argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
+    _check(_lib.load().pa_decode_append(*argv), "pa_decode_append")
 
 
 def pa_decode_shared_prefix(*args, group_start, group_prefix, max_group_size, max_prefix_len, **kw):

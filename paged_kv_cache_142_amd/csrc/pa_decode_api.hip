@@ -301,6 +301,8 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.plan = (int*)((char*)workspace + plan_offset(num_seqs, num_heads, head_dim, max_parts));
     a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
     a.skip_parts = nullptr;
+    a.new_k = nullptr;
+    a.new_v = nullptr;
     pr.head_dim = head_dim;
     pr.group = group;
     pr.kv_dtype = kv_dtype;
@@ -321,6 +323,45 @@ static int run_partition(const Prepared& pr, hipStream_t stream) {
         case PA_DTYPE_FP8_E4M3: return launch_partition_fp8_bf16q(pr.args, pr.head_dim, pr.group, stream);
     }
     return PA_ERR_DTYPE;
+}
+
+// Decode with append, for shapes whose partition kernel does not store the
+// new tokens itself: one workgroup per sequence copies the K and V rows of
+// its newest token (position seq_lens - 1) into that position's slot, as
+// pa_reshape_and_cache would with the slot taken from the block table.
+// Sequences with an invalid length or block id are skipped.
+__global__ void __launch_bounds__(256) append_tokens_kernel(const u32x4* __restrict__ key,
+                                                             const u32x4* __restrict__ value, u32x4* k_cache,
+                                                             u32x4* v_cache, const DecodeArgs a, int granules_per_row) {
+    const int seq = blockIdx.x;
+    const int T = a.seq_lens[seq];
+    const int B = a.block_size;
+    if (T <= 0 || T > a.max_seq_len || (T + B - 1) / B > a.max_blocks_per_seq) return;
+    const int pb = a.block_tables[(size_t)seq * a.max_blocks_per_seq + (T - 1) / B];
+    if (pb < 0 || pb >= a.num_blocks) return;
+    const int row = (T - 1) % B;
+    const int per_tensor = a.num_kv_heads * granules_per_row;
+    for (int i = threadIdx.x; i < 2 * per_tensor; i += blockDim.x) {
+        const int which = i / per_tensor;  // 0 = K, 1 = V
+        const int hg = i - which * per_tensor;
+        const int h = hg / granules_per_row;
+        const int g = hg - h * granules_per_row;
+        const size_t src = ((size_t)seq * a.num_kv_heads + h) * granules_per_row + g;
+        const size_t dst = (((size_t)pb * a.num_kv_heads + h) * B + row) * granules_per_row + g;
+        if (which == 0)
+            k_cache[dst] = key[src];
+        else
+            v_cache[dst] = value[src];
+    }
+}
+
+// Shapes whose partition kernel stores the new tokens itself (the GQA-4 kernel).
+static bool partition_appends(const Prepared& pr) {
+#ifdef PA_DISABLE_GQA4
+    return false;
+#else
+    return (pr.kv_dtype == PA_DTYPE_BF16 || pr.kv_dtype == PA_DTYPE_F16) && pr.group == 4;
+#endif
 }
 
 static int run_reduce(const Prepared& pr, hipStream_t stream) {
@@ -389,6 +430,29 @@ extern "C" int pa_decode(PA_DECODE_PARAMS) {
     const int s1 = pa::run_partition(pr, (hipStream_t)stream);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, (hipStream_t)stream);
+}
+
+extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* value) {
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    if (!key || !value) return PA_ERR_NULL;
+    if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_SHAPE;
+    PA_CHECK_SEQUENCES();
+    const hipStream_t s = (hipStream_t)stream;
+    if (pa::partition_appends(pr)) {
+        pr.args.new_k = key;
+        pr.args.new_v = value;
+    } else {
+        const int granules = head_dim * (kv_dtype == PA_DTYPE_F32 ? 4 : kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2) / 16;
+        using pa::u32x4;
+        hipLaunchKernelGGL(pa::append_tokens_kernel, dim3((unsigned)num_seqs), dim3(256), 0, s, (const u32x4*)key,
+                           (const u32x4*)value, (u32x4*)k_cache, (u32x4*)v_cache, pr.args, granules);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+    }
+    const int s1 = pa::run_partition(pr, s);
+    if (s1 != PA_OK) return s1;
+    return pa::run_reduce(pr, s);
 }
 
 extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_start, const int32_t* group_prefix,

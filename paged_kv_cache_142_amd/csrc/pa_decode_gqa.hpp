@@ -55,7 +55,8 @@ struct GqaShape {
     static constexpr int VPASS = 16 / R;
     static constexpr int SCRATCH = 512;      // p[16][G] + alpha[G], padded
     static constexpr int QBYTES = G * D * 2; // the group's query rows
-    static constexpr int RING = S * STAGE + SCRATCH + QBYTES;
+    static constexpr int NEWROW = 2 * ROWB;  // an appended token's K and V rows
+    static constexpr int RING = S * STAGE + SCRATCH + QBYTES + NEWROW;
     static constexpr int MERGE_HEAD = ((2 * W * G + W) * 4 + 15) / 16 * 16;
     static constexpr int MERGE = MERGE_HEAD + W * R * G * D * 4;
     static constexpr int LDS = (W * RING > MERGE) ? W * RING : MERGE;
@@ -130,6 +131,14 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     const int hq0 = kvh * G;
     const float qk_scale = a.qk_scale_log2;
 
+    // Decode with append: the wave that stages the sequence's last block
+    // copies the newest token's K and V rows of this kv head to LDS with its
+    // first copies, writes them over that row of the staged tile once the tile
+    // has landed, and stores them into the pool.  The attention thus never
+    // depends on when the store reaches memory.
+    const bool appends = a.new_k != nullptr && part == n_parts - 1 && nbw > 0 && kb0 + nbw == nblk;
+    const int new_row = (T - 1) % BS;
+
     // Source offset of this lane's 16 bytes in each 1 KiB copy of a K tile
     // (swizzled) and a V tile (natural order); the same for every block.
     uint32_t koff[Sh::DMA_PER_TILE];
@@ -155,6 +164,13 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     if (nbw > 0 && lane * 16 < Sh::QBYTES)
         dma16_to_lds((const char*)a.q + ((size_t)seq * a.num_heads + hq0) * D * 2 + lane * 16,
                      ring_lds + (uint32_t)(S * Sh::STAGE + Sh::SCRATCH));
+    const char* new_lds = ring + S * Sh::STAGE + Sh::SCRATCH + Sh::QBYTES;  // [K row][V row]
+    if (appends && lane < NG) {
+        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * ROWB + lane * 16;
+        const uint32_t at = ring_lds + (uint32_t)(S * Sh::STAGE + Sh::SCRATCH + Sh::QBYTES);
+        dma16_to_lds((const char*)a.new_k + src, at);
+        dma16_to_lds((const char*)a.new_v + src, at + ROWB);
+    }
     uint32_t qw[Sh::QW];
     auto load_q = [&]() {
         const char* qrow = q_lds + (hl * D + half * (D / 2)) * 2;
@@ -274,6 +290,21 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
         if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
         wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
         if (k == 0) load_q();
+        if (appends && k == nbw - 1) {
+            const int pb = nblk - 1 < 64 ? __builtin_amdgcn_readlane(ids, nblk - 1) : bt[nblk - 1];
+            if (lane < NG) {
+                const u32x4 kg = *(const u32x4*)(new_lds + lane * 16);
+                const u32x4 vg = *(const u32x4*)(new_lds + ROWB + lane * 16);
+                char* row = ring + stage * Sh::STAGE + new_row * ROWB;
+                *(u32x4*)(row + ((lane ^ (new_row & (NG - 1))) * 16)) = kg;  // K granules are swizzled
+                *(u32x4*)(row + TILE + lane * 16) = vg;
+                if ((unsigned)pb < (unsigned)a.num_blocks) {
+                    const size_t dst = ((size_t)pb * a.num_kv_heads + kvh) * TILE + new_row * ROWB + lane * 16;
+                    *(u32x4*)((char*)a.k_cache + dst) = kg;
+                    *(u32x4*)((char*)a.v_cache + dst) = vg;
+                }
+            }
+        }
         const char* sp = ring + stage * Sh::STAGE;
         const int blk_tok0 = (lb0 + kb0 + k) * BS;
         if (blk_tok0 + BS <= T) {

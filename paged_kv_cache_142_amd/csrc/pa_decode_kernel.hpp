@@ -74,6 +74,12 @@ struct DecodeArgs {
     // prefix of its group, by the prefix kernel); nullptr: none.  Those
     // partitions have no items here; their states are in the workspace.
     const int32_t* skip_parts;
+    // Decode with append: the K and V rows [num_seqs][num_kv_heads][head_dim]
+    // of each sequence's newest token (position seq_lens - 1), stored into
+    // its slot by the workgroup that owns the sequence's last partition;
+    // nullptr: the tokens are already in the pool.
+    const void* new_k;
+    const void* new_v;
 };
 
 constexpr int PLAN_ITEMS_OFFSET = 64;

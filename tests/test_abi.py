@@ -179,6 +179,33 @@ def test_decode_validation(lib, fn):
     assert _dec(lib, fn, ws_bytes=need - 1) == WS
 
 
+def _append(lib, key=FAKE, value=FAKE, **kw):
+    a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, k_cache=FAKE, v_cache=FAKE, kv_dtype=BF16,
+             tables=FAKE, max_blocks=256, seq_lens=FAKE, max_seq_len=4096, num_seqs=64, heads=32, kv_heads=8,
+             dim=128, block=16, blocks=9000, scale=0.088, k_scale=None, v_scale=None, part=512, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.pa_decode_append(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k_cache"], a["v_cache"],
+                                a["kv_dtype"], a["tables"], a["max_blocks"], a["seq_lens"], a["max_seq_len"],
+                                a["num_seqs"], a["heads"], a["kv_heads"], a["dim"], a["block"], a["blocks"],
+                                ctypes.c_float(a["scale"]), a["k_scale"], a["v_scale"], a["part"], a["ws"],
+                                a["ws_bytes"], None, key, value)
+
+
+def test_decode_append_validation(lib):
+    # pa_decode's checks first, then the new rows; all return before any launch
+    assert _append(lib, num_seqs=0) == OK
+    assert _append(lib, q_dtype=F16) == DTYPE
+    assert _append(lib, heads=24, kv_heads=8) == UNSUP
+    assert _append(lib, out=None) == NULL
+    need = lib.pa_decode_workspace_size(64, 32, 128, 4096, 512)
+    assert _append(lib, ws_bytes=need - 1) == WS
+    assert _append(lib, key=None) == NULL
+    assert _append(lib, value=None) == NULL
+    assert _append(lib, key=FAKE + 8) == SHAPE  # misaligned
+    assert _append(lib, value=FAKE + 4) == SHAPE
+
+
 def _sp(lib, gs=FAKE, gp=FAKE, groups=4, mgs=16, mpl=1024, **kw):
     a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, k_cache=FAKE, v_cache=FAKE, kv_dtype=BF16,
              tables=FAKE, max_blocks=256, seq_lens=FAKE, max_seq_len=4096, num_seqs=64, heads=32, kv_heads=8,

@@ -25,6 +25,7 @@ from .generators import (  # noqa: F401
     DecodeWorkload,
     PrefillWorkload,
     SharedPrefixWorkload,
+    build_decode_workload,
     build_prefill_workload,
     gqa,
     long_fp8,

@@ -295,7 +295,8 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
  * pa_reshape_and_cache followed by pa_decode.
  *
  * For the GQA-4 kernel's shapes (bf16 or f16 K/V, four query heads per kv
- * head) the store happens inside the partition kernel: the workgroup that
+ * head, at most 64 blocks per partition) the store happens inside the
+ * partition kernel: the workgroup that
  * owns a sequence's last partition copies the new rows into the pool and
  * into its staged tile, saving the separate scatter launch.  Other shapes
  * launch a small copy kernel first.

@@ -59,7 +59,9 @@ def load(path: str = None):
             "(the HIP library is required; there is no CPU path)")
     lib = ctypes.CDLL(path)
     for name, (restype, argtypes) in SIGNATURES.items():
-        fn = getattr(lib, name)
+        fn = getattr(lib, name, None)
+        if fn is None:  # an older build without this entry point: calling it raises AttributeError
+            continue
         fn.restype = restype
         fn.argtypes = argtypes
     _libs[path] = lib

@@ -355,12 +355,15 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(const u32x4* __restr
     }
 }
 
-// Shapes whose partition kernel stores the new tokens itself (the GQA-4 kernel).
+// Shapes whose partition kernel stores the new tokens itself: the GQA-4
+// kernel, when a partition has at most 64 blocks (their ids sit in one
+// vector register).
 static bool partition_appends(const Prepared& pr) {
 #ifdef PA_DISABLE_GQA4
     return false;
 #else
-    return (pr.kv_dtype == PA_DTYPE_BF16 || pr.kv_dtype == PA_DTYPE_F16) && pr.group == 4;
+    return (pr.kv_dtype == PA_DTYPE_BF16 || pr.kv_dtype == PA_DTYPE_F16) && pr.group == 4 &&
+           pr.args.partition_size / pr.args.block_size <= 64;
 #endif
 }
 

@@ -55,14 +55,15 @@ struct GqaShape {
     static constexpr int VPASS = 16 / R;
     static constexpr int SCRATCH = 512;      // p[16][G] + alpha[G], padded
     static constexpr int QBYTES = G * D * 2; // the group's query rows
-    static constexpr int NEWROW = 2 * ROWB;  // an appended token's K and V rows
-    static constexpr int RING = S * STAGE + SCRATCH + QBYTES + NEWROW;
+    static constexpr int RING = S * STAGE + SCRATCH + QBYTES;
     static constexpr int MERGE_HEAD = ((2 * W * G + W) * 4 + 15) / 16 * 16;
     static constexpr int MERGE = MERGE_HEAD + W * R * G * D * 4;
     static constexpr int LDS = (W * RING > MERGE) ? W * RING : MERGE;
+    static constexpr int NEWROW = 2 * ROWB;           // an appended token's K and V rows, per wave
+    static constexpr int LDS_APPEND = LDS + W * NEWROW;  // after everything else
     static_assert(TILE % 1024 == 0, "a tile must be a whole number of 1 KiB wave copies");
     static_assert((S - 1) * DMA_PER_BLOCK <= 63, "vmcnt can count at most 63 copies");
-    static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+    static_assert(LDS_APPEND <= 160 * 1024, "LDS budget of one CU");
     static_assert(G * 2 * TQ == 64, "lane decomposition");
 };
 
@@ -85,7 +86,7 @@ __device__ __forceinline__ float dpp_max(float x) {
 #endif
 
 // At least PA_GQA_WAVES_PER_SIMD waves per SIMD: caps registers at 168.
-template <Fmt KV, int D, int BS, int W, int S>
+template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
 __global__ void __launch_bounds__(W * 64, PA_GQA_WAVES_PER_SIMD)
 decode_partition_gqa4_kernel(const DecodeArgs a) {
     using Sh = GqaShape<KV, D, BS, W, S>;
@@ -136,7 +137,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     // first copies, writes them over that row of the staged tile once the tile
     // has landed, and stores them into the pool.  The attention thus never
     // depends on when the store reaches memory.
-    const bool appends = a.new_k != nullptr && part == n_parts - 1 && nbw > 0 && kb0 + nbw == nblk;
+    const bool appends = APPEND && part == n_parts - 1 && nbw > 0 && kb0 + nbw == nblk;
     const int new_row = (T - 1) % BS;
 
     // Source offset of this lane's 16 bytes in each 1 KiB copy of a K tile
@@ -164,10 +165,10 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     if (nbw > 0 && lane * 16 < Sh::QBYTES)
         dma16_to_lds((const char*)a.q + ((size_t)seq * a.num_heads + hq0) * D * 2 + lane * 16,
                      ring_lds + (uint32_t)(S * Sh::STAGE + Sh::SCRATCH));
-    const char* new_lds = ring + S * Sh::STAGE + Sh::SCRATCH + Sh::QBYTES;  // [K row][V row]
+    const char* new_lds = smem + Sh::LDS + wave * Sh::NEWROW;  // [K row][V row]
     if (appends && lane < NG) {
         const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * ROWB + lane * 16;
-        const uint32_t at = ring_lds + (uint32_t)(S * Sh::STAGE + Sh::SCRATCH + Sh::QBYTES);
+        const uint32_t at = lds_addr_of(smem) + (uint32_t)(Sh::LDS + wave * Sh::NEWROW);
         dma16_to_lds((const char*)a.new_k + src, at);
         dma16_to_lds((const char*)a.new_v + src, at + ROWB);
     }
@@ -183,7 +184,9 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
 
     auto issue = [&](int k, int stage) {
         const int idx = kb0 + k;  // block index inside the partition
-        int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : bt[idx];
+        // a uniform id (kept in a scalar register: a vector register that a
+        // pending table load may still write would make later copies wait)
+        int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : __builtin_amdgcn_readfirstlane(bt[idx]);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
@@ -291,7 +294,8 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
         wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
         if (k == 0) load_q();
         if (appends && k == nbw - 1) {
-            const int pb = nblk - 1 < 64 ? __builtin_amdgcn_readlane(ids, nblk - 1) : bt[nblk - 1];
+            // the host appends here only when a partition has at most 64 blocks
+            const int pb = __builtin_amdgcn_readlane(ids, min(nblk - 1, 63));
             if (lane < NG) {
                 const u32x4 kg = *(const u32x4*)(new_lds + lane * 16);
                 const u32x4 vg = *(const u32x4*)(new_lds + ROWB + lane * 16);
@@ -366,16 +370,25 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     }
 }
 
-template <Fmt KV, int D, int BS, int W, int S>
-int launch_partition_gqa4(const DecodeArgs& a, hipStream_t stream) {
+template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
+int launch_partition_gqa4_as(const DecodeArgs& a, hipStream_t stream) {
     using Sh = GqaShape<KV, D, BS, W, S>;
-    auto kernel = decode_partition_gqa4_kernel<KV, D, BS, W, S>;
+    constexpr int LDS = APPEND ? Sh::LDS_APPEND : Sh::LDS;
+    auto kernel = decode_partition_gqa4_kernel<KV, D, BS, W, S, APPEND>;
     static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
     const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
-    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
+    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// The plain kernel, or the one that also stores the new tokens (decode with
+// append): separate instantiations, so that the plain one carries none of it.
+template <Fmt KV, int D, int BS, int W, int S>
+int launch_partition_gqa4(const DecodeArgs& a, hipStream_t stream) {
+    return a.new_k != nullptr ? launch_partition_gqa4_as<KV, D, BS, W, S, true>(a, stream)
+                              : launch_partition_gqa4_as<KV, D, BS, W, S, false>(a, stream);
 }
 
 #ifndef PA_GQA_WAVES

@@ -70,10 +70,11 @@ def _replays_match(g, out, eager, what, reps=4):
         assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"{what}: replay {rep} differs"
 
 
-@pytest.mark.parametrize("kind", ["fp8_quantize", "plan_kernel"])
+@pytest.mark.parametrize("kind", ["fp8_quantize", "plan_kernel", "append"])
 def test_graph_other_decode_paths(kind):
-    """The FP8 step (quantize-on-write scatter, matrix-core decode) and a
-    batch of more than 64 sequences (work order from the plan kernel)."""
+    """The FP8 step (quantize-on-write scatter, matrix-core decode), a batch
+    of more than 64 sequences (work order from the plan kernel), and the
+    step as copies plus decode with append."""
     if kind == "fp8_quantize":
         wl = workloads.long_fp8(8, num_seqs=3, seq_len=1500, partition_size=512)
     else:
@@ -86,6 +87,9 @@ def test_graph_other_decode_paths(kind):
     args = case.decode_args()
 
     def calls():
+        if kind == "append":
+            return [pa.prepared("pa_copy_blocks", case.k_cache, case.v_cache, case.pairs),
+                    pa.prepared("pa_decode_append", **args, key=case.step_keys, value=case.step_values)]
         if case.quantize_step:
             first = pa.prepared("pa_reshape_and_cache_fp8", case.step_keys, case.step_values, case.k_cache,
                                 case.v_cache, case.k_scale, case.v_scale, case.step_slots)

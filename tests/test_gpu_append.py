@@ -86,3 +86,36 @@ def test_append_gqa_workload_and_oracle():
 def test_append_plan_kernel_order():
     # more than 64 sequences: the work order comes from the plan kernel
     _compare(workloads.gqa(5, num_seqs=90, max_len=1200, partition_size=256))
+
+
+@pytest.mark.parametrize("heads,kv_heads", [(32, 8), (16, 16)])
+def test_append_invalid_last_block_stores_nothing(heads, kv_heads):
+    """A sequence whose last block id lies outside the pool gets a NaN row and
+    no store; the other sequences are unaffected (fused and copy-kernel paths)."""
+    wl = workloads.build_decode_workload(f"append_bad_{heads}_{kv_heads}", 33, seq_lens=[300, 40, 1000, 17],
+                                         num_heads=heads, num_kv_heads=kv_heads, head_dim=128, block_size=16,
+                                         kv_dtype="bf16", q_dtype="bf16", spare_blocks=4, num_copy_pairs=0,
+                                         partition_size=256)
+    print(f"[case] append with an out-of-pool block, H={heads}/{kv_heads}", flush=True)
+    case = DeviceCase(wl)
+    torch.cuda.synchronize()
+    before_k, before_v = _bytes(case.k_cache), _bytes(case.v_cache)
+    bad = wl.block_tables.copy()
+    bad[2, (1000 - 1) // 16] = wl.num_blocks + 5
+    keys = case.keys.index_select(0, case.step).contiguous()
+    values = case.values.index_select(0, case.step).contiguous()
+    pa.pa_decode_append(**case.decode_args(block_tables=torch.from_numpy(bad).cuda()), key=keys, value=values)
+    torch.cuda.synchronize()
+    out = out_as_f64(case.out)
+    assert np.isnan(out[2]).all() and np.isfinite(out[[0, 1, 3]]).all()
+    # only the three valid sequences' new rows changed in the pools
+    slots = set()
+    for i in (0, 1, 3):
+        T = int(wl.seq_lens[i])
+        slots.add(int(wl.block_tables[i, (T - 1) // 16]) * 16 + (T - 1) % 16)
+    for before, after in ((before_k, _bytes(case.k_cache)), (before_v, _bytes(case.v_cache))):
+        elems = np.nonzero(after.reshape(-1).view(np.uint16) != before.reshape(-1).view(np.uint16))[0]
+        blk = elems // (kv_heads * 16 * 128)
+        row = (elems % (16 * 128)) // 128
+        assert len(elems) == len(slots) * kv_heads * 128
+        assert set((blk * 16 + row).tolist()) == slots

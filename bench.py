@@ -3,13 +3,13 @@
 A step is one pass of the whole path over the batch: the step's block
 copies (``pa_copy_blocks``), the scatter of each sequence's new token into
 the pool, and the decode itself.  Where one call can do the last two
-(bf16/f16/f32 pools decoded with ``pa_decode``), the step is
-``pa_copy_blocks`` then ``pa_decode_append``, which stores the tokens inside
-the partition kernel for four query heads per kv head; otherwise (FP8 pools
-quantized on write, grouped shared-prefix decode) it is the scatter
-(``pa_reshape_and_cache[_fp8]``), the copies, and the decode
-(``pa_decode_partition`` then ``pa_decode_reduce``, or
-``pa_decode_shared_prefix``).  ``step_calls`` in the output names them.
+(bf16/f16/f32 pools), the step is ``pa_copy_blocks`` then
+``pa_decode_append`` (or ``pa_decode_shared_prefix`` given the new tokens,
+for the grouped shared-prefix workloads), which stores the tokens inside the
+partition kernel for four query heads per kv head; for FP8 pools (quantized
+on write) it is the scatter (``pa_reshape_and_cache_fp8``), the copies, and
+the decode (``pa_decode_partition`` then ``pa_decode_reduce``).
+``step_calls`` in the output names them.
 Inputs are resident in HBM before the timed region.  Throughput is the
 effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
 By default two copies of the K/V pool alternate between steps, so that no
@@ -383,8 +383,7 @@ class Device:
         # (pa_decode_append: copy-on-write copies first, then one call) where
         # that call applies; the per-call timing loop keeps the four separate
         # launches (scatter, copy, partition, reduce).
-        self.append_fused = (groups is None and not self.quantize_step
-                             and self.step_keys.shape[0] == wl.num_seqs)
+        self.append_fused = not self.quantize_step and self.step_keys.shape[0] == wl.num_seqs
         # identical calls every step: marshal the C arguments once per pool copy
         self.call_sets = [self._make_calls(kc, vc, fused=self.append_fused) for kc, vc in self.pools]
         self.part_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
@@ -406,6 +405,9 @@ class Device:
         if fused:
             copy = pa.prepared("pa_copy_blocks", kc, vc, self.pairs, kv_dtype=kv) if self.pairs.numel() else (
                 lambda: None)
+            if self.groups is not None:
+                return [copy, pa.prepared("pa_decode_shared_prefix", **dargs, **self.groups, key=self.step_keys,
+                                          value=self.step_values)]
             return [copy, pa.prepared("pa_decode_append", **dargs, key=self.step_keys, value=self.step_values)]
         scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, kc, vc,
                                self.k_scale, self.v_scale, self.step_slots)
@@ -539,8 +541,13 @@ def main():
         starts = np.arange(0, wl.num_seqs + 1, beams, dtype=np.int32)
         prompt_len = (1032 if args.config.startswith("shared_prefix_cow") else
                       LONG_PROMPT if args.config.startswith("shared_prefix_long") else 1024)
-        shared = prompt_len // wl.block_size * wl.block_size
-        groups = (starts, np.full(len(starts) - 1, shared, np.int32))
+        # the prompt's whole blocks, and never a member's newest token (which
+        # the step stores into the member's own block): a beam with no suffix
+        # yet shares one block less
+        B = wl.block_size
+        shared = np.array([min(prompt_len // B * B, int((wl.seq_lens[a:b] - 1).min()) // B * B)
+                           for a, b in zip(starts[:-1], starts[1:])], np.int32)
+        groups = (starts, shared)
     dev = Device(wl, pools=args.pools, groups=groups)
     graph = None
     if args.graph:  # one eager step first (one-time kernel attribute setup), then capture
@@ -631,7 +638,8 @@ def main():
             [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
-        "step_calls": (["pa_copy_blocks", "pa_decode_append"] if dev.append_fused else
+        "step_calls": (["pa_copy_blocks", "pa_decode_shared_prefix (with the new tokens)" if groups is not None
+                        else "pa_decode_append"] if dev.append_fused else
                        ["pa_reshape_and_cache" + ("_fp8" if dev.quantize_step else ""), "pa_copy_blocks",
                         "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
                         *([] if groups is not None else ["pa_decode_reduce"])]),

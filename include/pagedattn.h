@@ -341,6 +341,10 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
  *   max_group_size, max_prefix_len   host bounds that size the grid: members
  *                 past the first max_group_size of a group are computed alone,
  *                 and prefixes are shared up to max_prefix_len tokens
+ *   key, value    optional (both NULL, or both set): each sequence's newest
+ *                 token, stored first as by pa_decode_append; that token must
+ *                 lie past its group's shared tokens (its block is the
+ *                 sequence's own)
  *   other arguments: as for pa_decode (same workspace size).
  * A member holding fewer tokens than its group's shared partitions is
  * computed alone; so is a whole group whose first sequence is that short.
@@ -355,7 +359,7 @@ int pa_decode_shared_prefix(void* out, int out_dtype, const void* q, int q_dtype
                             float scale, const float* k_scale, const float* v_scale, int partition_size,
                             void* workspace, size_t workspace_bytes, void* stream, const int32_t* group_start,
                             const int32_t* group_prefix, int num_groups, int max_group_size,
-                            int max_prefix_len);
+                            int max_prefix_len, const void* key, const void* value);
 
 /*
  * pa_prefill -- multi-query (prefill or chunked prefill) attention over the

@@ -158,7 +158,9 @@ def prepared(name, *args, **kw):
         argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
     elif name == "pa_decode_shared_prefix":
         gs, gp, mgs, mpl = (kw.pop(k) for k in ("group_start", "group_prefix", "max_group_size", "max_prefix_len"))
-        argv = _decode_argv(*args, **kw) + _group_argv(gs, gp, mgs, mpl)
+        key, value = kw.pop("key", None), kw.pop("value", None)
+        argv = (_decode_argv(*args, **kw) + _group_argv(gs, gp, mgs, mpl)
+                + (_append_argv(key, value, args, kw) if key is not None else (None, None)))
     elif name == "pa_prefill":
         argv = _prefill_argv(*args, **kw)
     elif name == "pa_reshape_and_cache":
@@ -221,13 +223,15 @@ def pa_decode_append(*args, key, value, **kw):
     _check(_lib.load().pa_decode_append(*argv), "pa_decode_append")
 
 
-def pa_decode_shared_prefix(*args, group_start, group_prefix, max_group_size, max_prefix_len, **kw):
+def pa_decode_shared_prefix(*args, group_start, group_prefix, max_group_size, max_prefix_len, key=None, value=None,
+                            **kw):
     """``pa_decode`` reading each group's shared prompt partitions once.
 
     ``group_start`` (int32, ``[G+1]``) and ``group_prefix`` (int32, ``[G]``
     shared tokens) are device tensors; the other arguments are ``pa_decode``'s.
     """
-    argv = _decode_argv(*args, **kw) + _group_argv(group_start, group_prefix, max_group_size, max_prefix_len)
+    argv = (_decode_argv(*args, **kw) + _group_argv(group_start, group_prefix, max_group_size, max_prefix_len)
+            + (_append_argv(key, value, args, kw) if key is not None else (None, None)))
     _check(_lib.load().pa_decode_shared_prefix(*argv), "pa_decode_shared_prefix")
 
 

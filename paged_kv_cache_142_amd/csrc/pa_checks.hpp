@@ -10,8 +10,9 @@
 //     max_blocks_per_seq blocks, and every table entry a sequence reads
 //     naming a block of the pool;
 //   - groups: group_start non-decreasing from 0 to num_seqs, prefixes not
-//     negative, and every member's table naming its group's first sequence's
-//     blocks for the tokens they share;
+//     negative, every member's table naming its group's first sequence's
+//     blocks for the tokens they share, and (when the call appends) every
+//     member's newest token past the shared tokens;
 //   - prefill queries: query_start non-decreasing from 0 to total_q, and
 //     each sequence's query count at most max_query_len and its length.
 // The copies make these calls synchronous, so the checked build is for
@@ -111,9 +112,11 @@ inline int sequences(const int32_t* seq_lens, const int32_t* block_tables, int n
 }
 
 // `lens` and `tables` as returned by sequences().
+// appending: the call also stores each sequence's newest token, which must
+// then lie past its group's shared tokens.
 inline int groups(const int32_t* group_start, const int32_t* group_prefix, int num_groups, int num_seqs,
                   int max_blocks_per_seq, int block_size, const std::vector<int32_t>& lens,
-                  const std::vector<int32_t>& tables, hipStream_t stream) {
+                  const std::vector<int32_t>& tables, bool appending, hipStream_t stream) {
     std::vector<int32_t> start, prefix;
     int st = fetch(start, group_start, (size_t)num_groups + 1, stream);
     if (st != PA_OK) return st;
@@ -124,6 +127,9 @@ inline int groups(const int32_t* group_start, const int32_t* group_prefix, int n
         if (start[g + 1] < start[g] || prefix[g] < 0) return PA_ERR_CONTENT;
         if (start[g + 1] == start[g]) continue;
         const int lead = start[g];
+        if (appending)
+            for (int i = lead; i < start[g + 1]; ++i)
+                if (lens[i] > 0 && lens[i] - 1 < prefix[g]) return PA_ERR_CONTENT;
         for (int i = lead + 1; i < start[g + 1]; ++i) {
             // the blocks holding the tokens both sequences have of the shared prefix
             const int shared = std::min(prefix[g], std::min(lens[i], lens[lead]));

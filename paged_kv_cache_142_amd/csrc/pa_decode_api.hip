@@ -435,6 +435,23 @@ extern "C" int pa_decode(PA_DECODE_PARAMS) {
     return pa::run_reduce(pr, (hipStream_t)stream);
 }
 
+namespace pa {
+// Arrange for the partition launch to store the newest tokens (key, value),
+// or store them now with the copy kernel when that kernel does not.
+static int prepare_append(Prepared& pr, const void* key, const void* value, void* k_cache, void* v_cache,
+                          int head_dim, hipStream_t s) {
+    if (partition_appends(pr)) {
+        pr.args.new_k = key;
+        pr.args.new_v = value;
+        return PA_OK;
+    }
+    const int eb = pr.kv_dtype == PA_DTYPE_F32 ? 4 : pr.kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2;
+    hipLaunchKernelGGL(append_tokens_kernel, dim3((unsigned)pr.args.num_seqs), dim3(256), 0, s, (const u32x4*)key,
+                       (const u32x4*)value, (u32x4*)k_cache, (u32x4*)v_cache, pr.args, head_dim * eb / 16);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+}  // namespace pa
+
 extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* value) {
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
@@ -443,28 +460,23 @@ extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* v
     if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_SHAPE;
     PA_CHECK_SEQUENCES();
     const hipStream_t s = (hipStream_t)stream;
-    if (pa::partition_appends(pr)) {
-        pr.args.new_k = key;
-        pr.args.new_v = value;
-    } else {
-        const int granules = head_dim * (kv_dtype == PA_DTYPE_F32 ? 4 : kv_dtype == PA_DTYPE_FP8_E4M3 ? 1 : 2) / 16;
-        using pa::u32x4;
-        hipLaunchKernelGGL(pa::append_tokens_kernel, dim3((unsigned)num_seqs), dim3(256), 0, s, (const u32x4*)key,
-                           (const u32x4*)value, (u32x4*)k_cache, (u32x4*)v_cache, pr.args, granules);
-        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-    }
+    const int s0 = pa::prepare_append(pr, key, value, (void*)k_cache, (void*)v_cache, head_dim, s);
+    if (s0 != PA_OK) return s0;
     const int s1 = pa::run_partition(pr, s);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, s);
 }
 
 extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_start, const int32_t* group_prefix,
-                                       int num_groups, int max_group_size, int max_prefix_len) {
+                                       int num_groups, int max_group_size, int max_prefix_len, const void* key,
+                                       const void* value) {
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
     if (st != PA_OK || pr.nothing_to_do) return st;
     if (num_groups < 0 || max_group_size < 0 || max_prefix_len < 0) return PA_ERR_SHAPE;
     if (num_groups > 0 && (!group_start || !group_prefix)) return PA_ERR_NULL;
+    if (!key != !value) return PA_ERR_NULL;  // both or neither
+    if (key && (!pa::aligned16(key) || !pa::aligned16(value))) return PA_ERR_SHAPE;
     const hipStream_t s = (hipStream_t)stream;
 #if PA_CHECK_CONTENTS
     {
@@ -473,10 +485,14 @@ extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_st
                                            block_size, num_blocks, lens, tables, s);
         if (checked == PA_OK && num_groups > 0)
             checked = pa::check::groups(group_start, group_prefix, num_groups, num_seqs, max_blocks_per_seq,
-                                        block_size, lens, tables, s);
+                                        block_size, lens, tables, key != nullptr, s);
         if (checked != PA_OK) return checked;
     }
 #endif
+    if (key) {
+        const int sa = pa::prepare_append(pr, key, value, (void*)k_cache, (void*)v_cache, head_dim, s);
+        if (sa != PA_OK) return sa;
+    }
     // nothing to share, or a shape the matrix-core tile does not cover: plain decode
     if (num_groups == 0 || max_prefix_len < partition_size || max_group_size == 0 || ((uintptr_t)out & 15u) ||
         !pa::prefix_states_supported(pr.kv_dtype, pr.q_dtype, pr.head_dim, block_size, pr.group)) {

@@ -216,7 +216,7 @@ def _sp(lib, gs=FAKE, gp=FAKE, groups=4, mgs=16, mpl=1024, **kw):
                                        a["kv_dtype"], a["tables"], a["max_blocks"], a["seq_lens"], a["max_seq_len"],
                                        a["num_seqs"], a["heads"], a["kv_heads"], a["dim"], a["block"], a["blocks"],
                                        ctypes.c_float(a["scale"]), a["k_scale"], a["v_scale"], a["part"], a["ws"],
-                                       a["ws_bytes"], None, gs, gp, groups, mgs, mpl)
+                                       a["ws_bytes"], None, gs, gp, groups, mgs, mpl, a.get("key"), a.get("value"))
 
 
 def test_shared_prefix_decode_validation(lib):
@@ -234,6 +234,10 @@ def test_shared_prefix_decode_validation(lib):
     assert _sp(lib, mpl=-1) == SHAPE
     assert _sp(lib, gs=None) == NULL
     assert _sp(lib, gp=None) == NULL
+    # the optional newest-token rows: both or neither, 16-byte aligned
+    assert _sp(lib, key=FAKE) == NULL
+    assert _sp(lib, value=FAKE) == NULL
+    assert _sp(lib, key=FAKE + 4, value=FAKE) == SHAPE
 
 
 def _pf(lib, **kw):

@@ -119,3 +119,46 @@ def test_append_invalid_last_block_stores_nothing(heads, kv_heads):
         row = (elems % (16 * 128)) // 128
         assert len(elems) == len(slots) * kv_heads * 128
         assert set((blk * 16 + row).tolist()) == slots
+
+
+@pytest.mark.parametrize("heads,kv_heads,fmt,block,P", [
+    (32, 8, "bf16", 16, 256),   # G = 4: the suffix partitions' kernel stores the token
+    (16, 16, "bf16", 16, 256),  # G = 1: copy kernel first
+    (32, 4, "f16", 32, 512),    # G = 8
+])
+def test_shared_prefix_decode_with_append(heads, kv_heads, fmt, block, P):
+    """pa_decode_shared_prefix given each sequence's newest token: the pools
+    and outputs of the same call over pools that already hold the tokens."""
+    from test_gpu_shared_prefix import _grouped_case
+    from gpu_util import poison_device, to_device
+
+    groups = [(2 * P, [2 * P + 5, 2 * P + 90, 2 * P + 1]), (P + 2 * block, [P + 2 * block + 1, P + 100]),
+              (0, [40, 300])]
+    lens, tables, starts, prefixes, hk, hv, q = _grouped_case(41, num_heads=heads, num_kv_heads=kv_heads,
+                                                              head_dim=128, block_size=block, fmt=fmt, groups=groups)
+    print(f"[case] shared-prefix decode with append H={heads}/{kv_heads} {fmt} B={block} P={P}", flush=True)
+    N, H, d = q.shape
+    msl = int(lens.max())
+    last_blk = np.array([tables[i, (int(T) - 1) // block] for i, T in enumerate(lens)])
+    last_row = (lens - 1) % block
+    new_k = np.stack([hk[b, :, r, :] for b, r in zip(last_blk, last_row)])
+    new_v = np.stack([hv[b, :, r, :] for b, r in zip(last_blk, last_row)])
+    grp = dict(group_start=torch.from_numpy(starts).cuda(), group_prefix=torch.from_numpy(prefixes).cuda(),
+               max_group_size=int(np.diff(starts).max()), max_prefix_len=int(prefixes.max()))
+    outs, pools = [], []
+    for append in (False, True):
+        kc, vc = to_device(hk, fmt), to_device(hv, fmt)
+        if append:  # the newest rows are not in the pool yet
+            for b, r in zip(last_blk, last_row):
+                kc[int(b), :, int(r), :] = float("nan")
+                vc[int(b), :, int(r), :] = float("nan")
+        out = poison_device((N, H, d), "f32")
+        ws = torch.empty(pa.pa_decode_workspace_size(N, H, d, msl, P), dtype=torch.uint8, device="cuda")
+        extra = dict(key=to_device(new_k, fmt), value=to_device(new_v, fmt)) if append else {}
+        pa.pa_decode_shared_prefix(out, to_device(q, fmt), kc, vc, torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(lens).cuda(), msl, 1.0 / np.sqrt(d), P, ws, **grp, **extra)
+        torch.cuda.synchronize()
+        outs.append(_bytes(out))
+        pools.append((_bytes(kc), _bytes(vc)))
+    assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
+    assert np.array_equal(outs[0], outs[1])

@@ -185,10 +185,11 @@ def test_shared_prefix_violations(checked):
                      device="cuda")
     out = poison_device(q.shape, "f32")
 
-    def call(t=tables, st=starts, pr=prefixes):
+    def call(t=tables, st=starts, pr=prefixes, **extra):
         pa.pa_decode_shared_prefix(out, qd, kc, vc, torch.from_numpy(t).cuda(), torch.from_numpy(lens).cuda(), msl,
                                    0.088, P, ws, group_start=torch.from_numpy(st).cuda(),
-                                   group_prefix=torch.from_numpy(pr).cuda(), max_group_size=3, max_prefix_len=2 * P)
+                                   group_prefix=torch.from_numpy(pr).cuda(), max_group_size=3, max_prefix_len=2 * P,
+                                   **extra)
 
     diverged = tables.copy()
     diverged[1, 5] = diverged[0, 5] + 1 if diverged[0, 5] + 1 < hk.shape[0] else diverged[0, 5] - 1
@@ -196,6 +197,9 @@ def test_shared_prefix_violations(checked):
     _rejects(lambda: call(st=np.array([0, 3, 4], np.int32)), "group_start not ending at num_seqs")
     _rejects(lambda: call(st=np.array([0, 6, 5], np.int32)), "group_start decreasing")
     _rejects(lambda: call(pr=np.array([2 * P, -1], np.int32)), "negative prefix")
+    rows = torch.zeros((q.shape[0], 8, 128), dtype=torch.bfloat16, device="cuda")
+    # the member of length 2P would store its newest token inside the shared 2P tokens
+    _rejects(lambda: call(key=rows, value=rows.clone()), "newest token inside the shared prefix")
     torch.cuda.synchronize()
     assert torch.isnan(out).all(), "a rejected call wrote the output"
     # past the shared prefix, members' tables may differ

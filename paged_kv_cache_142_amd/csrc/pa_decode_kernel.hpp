@@ -427,7 +427,11 @@ decode_partition_kernel(const DecodeArgs a) {
         for (int g = 0; g < G; ++g) qop[g].pin();
     }
     float qk_scale = a.qk_scale_log2;
-    if constexpr (KV == Fmt::FP8) qk_scale *= a.k_scale[kvh];
+    if constexpr (KV == Fmt::FP8) {
+        float ks = a.k_scale[kvh];
+        asm volatile("" : "+v"(ks));  // resident before the copies, like the queries
+        qk_scale *= ks;
+    }
 
     const char* kc = (const char*)a.k_cache;
     const char* vc = (const char*)a.v_cache;
@@ -436,7 +440,12 @@ decode_partition_kernel(const DecodeArgs a) {
     int invalid = 0;
 
     auto issue = [&](int k, int stage) {
-        if (k > 0 && (k & 63) == 0) ids = k + lane < nbw ? bt[k + lane] : 0;
+        if (k > 0 && (k & 63) == 0) {
+            ids = k + lane < nbw ? bt[k + lane] : 0;
+            // wait for the new ids here: otherwise the compiler waits (for every
+            // copy in flight) before each block's readlane, reloaded or not
+            asm volatile("" : "+v"(ids));
+        }
         int pb = __builtin_amdgcn_readlane(ids, k & 63);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)lane * 16;

@@ -142,6 +142,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     const int id_lim = min(min(P / BS, 64), a.max_blocks_per_seq - lb0);
     int ids = lane < id_lim ? bt[lane] : 0;
     const int T = a.seq_lens[seq];
+    float k_scale = a.k_scale[kvh];
     // Query operand: head n's elements 32 g .. 32 g + 31 (zero for n >= G).
     bf16x8 qop[Sh::NC];
     {
@@ -156,7 +157,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     }
     // make ids and queries resident before any asynchronous copy is queued:
     // the compiler does not see those copies and would otherwise wait for them
-    asm volatile("" : "+v"(ids));
+    asm volatile("" : "+v"(ids), "+v"(k_scale));
 #pragma unroll
     for (int c = 0; c < Sh::NC; ++c) asm volatile("" : "+v"(qop[c]));
     if (T <= 0 || T > a.max_seq_len) return;
@@ -170,7 +171,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     // this wave's steps: a contiguous, balanced share of the partition
     const int u0 = nunits * wave / W;
     const int nuw = nunits * (wave + 1) / W - u0;
-    const float qk_scale = a.qk_scale_log2 * a.k_scale[kvh];
+    const float qk_scale = a.qk_scale_log2 * k_scale;
 
     // Source offsets of this lane's 16 bytes in each 1 KiB copy of a K tile
     // and a V tile (the granule permutations depend only on the row inside

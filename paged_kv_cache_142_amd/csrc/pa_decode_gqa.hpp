@@ -85,9 +85,19 @@ __device__ __forceinline__ float dpp_max(float x) {
 #define PA_GQA_WAVES_PER_SIMD 3
 #endif
 
-// At least PA_GQA_WAVES_PER_SIMD waves per SIMD: caps registers at 168.
+// At most this many waves per SIMD in the launch bound (3 caps registers at 168).
+// Waves per SIMD that the LDS lets a CU hold for this shape, at most
+// PA_GQA_WAVES_PER_SIMD: the register budget of the launch bound.  Asking for
+// more than the LDS allows would only cap registers (and make the compiler
+// spill) without adding a wave.
+template <Fmt KV, int D, int BS, int W, int S>
+constexpr int gqa_waves_per_simd() {
+    constexpr int per_cu = (160 * 1024) / GqaShape<KV, D, BS, W, S>::LDS_APPEND * W / 4;
+    return per_cu < 1 ? 1 : per_cu > PA_GQA_WAVES_PER_SIMD ? PA_GQA_WAVES_PER_SIMD : per_cu;
+}
+
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
-__global__ void __launch_bounds__(W * 64, PA_GQA_WAVES_PER_SIMD)
+__global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
 decode_partition_gqa4_kernel(const DecodeArgs a) {
     using Sh = GqaShape<KV, D, BS, W, S>;
     using Row = LaneRow<KV, D>;

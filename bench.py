@@ -300,9 +300,9 @@ def _workload(name, seed, partition_size):
 def _describe(wl):
     return (f"{wl.name}: {wl.num_seqs} seqs, sum T={int(wl.seq_lens.sum())} (max {wl.max_seq_len}), "
             f"{wl.num_heads}/{wl.num_kv_heads} heads, d={wl.head_dim}, B={wl.block_size}, {wl.kv_dtype} KV, "
-            f"{wl.q_dtype} q, f32 out and accumulation, P={wl.partition_size}; step = scatter of "
-            f"{wl.num_seqs} new tokens{' (bf16, quantized on write)' if wl.step_keys_src is not None else ''}"
-            f" + copy of {len(wl.copy_pairs)} blocks + split-KV decode")
+            f"{wl.q_dtype} q, f32 out and accumulation, P={wl.partition_size}; step = copy of "
+            f"{len(wl.copy_pairs)} blocks + store of {wl.num_seqs} new tokens"
+            f"{' (bf16, quantized on write)' if wl.step_keys_src is not None else ''} + split-KV decode")
 
 
 def _first_per_slot(slots, rows):

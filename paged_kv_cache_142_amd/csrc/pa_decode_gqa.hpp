@@ -92,14 +92,18 @@ __device__ __forceinline__ float dpp_max(float x) {
 // spill) without adding a wave.
 template <Fmt KV, int D, int BS, int W, int S>
 constexpr int gqa_waves_per_simd() {
-    constexpr int per_cu = (160 * 1024) / GqaShape<KV, D, BS, W, S>::LDS_APPEND * W / 4;
+    constexpr int per_cu = (160 * 1024) / GqaShape<KV, D, 16, W, S>::LDS_APPEND * W / 4;
     return per_cu < 1 ? 1 : per_cu > PA_GQA_WAVES_PER_SIMD ? PA_GQA_WAVES_PER_SIMD : per_cu;
 }
 
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
 __global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
 decode_partition_gqa4_kernel(const DecodeArgs a) {
-    using Sh = GqaShape<KV, D, BS, W, S>;
+    // Tiles are staged 16 rows at a time whatever the pool's block size BS:
+    // a 32-token block is two 16-row halves, each a contiguous tile.
+    using Sh = GqaShape<KV, D, 16, W, S>;
+    constexpr int HALVES = BS / 16;
+    constexpr size_t POOL_TILE = (size_t)BS * D * 2;  // one (block, kv head) tile of the pool
     using Row = LaneRow<KV, D>;
     constexpr int G = Sh::G, NG = Sh::NG, ROWB = Sh::ROWB, TILE = Sh::TILE, TQ = Sh::TQ, R = Sh::R;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -135,7 +139,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     if (part >= n_parts) return;
     const int tok0 = part * P;
     const int tok1 = min(tok0 + P, T);
-    const int nblk = (tok1 - tok0 + BS - 1) / BS;
+    const int nblk = (tok1 - tok0 + 15) / 16;  // 16-row tiles of the partition (blocks when BS = 16)
     // this wave's blocks: a contiguous, balanced share of the partition
     const int kb0 = nblk * wave / W;
     const int nbw = nblk * (wave + 1) / W - kb0;
@@ -148,7 +152,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     // has landed, and stores them into the pool.  The attention thus never
     // depends on when the store reaches memory.
     const bool appends = APPEND && part == n_parts - 1 && nbw > 0 && kb0 + nbw == nblk;
-    const int new_row = (T - 1) % BS;
+    const int new_row = (T - 1) % 16;  // row of the newest token in its staged tile
 
     // Source offset of this lane's 16 bytes in each 1 KiB copy of a K tile
     // (swizzled) and a V tile (natural order); the same for every block.
@@ -193,12 +197,14 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     };
 
     auto issue = [&](int k, int stage) {
-        const int idx = kb0 + k;  // block index inside the partition
+        const int vidx = kb0 + k;         // 16-row tile inside the partition
+        const int idx = vidx / HALVES;    // its block inside the partition
         // a uniform id (kept in a scalar register: a vector register that a
         // pending table load may still write would make later copies wait)
         int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : __builtin_amdgcn_readfirstlane(bt[idx]);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
-        const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
+        size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * POOL_TILE;
+        if constexpr (HALVES > 1) tile += (size_t)(vidx % HALVES) * TILE;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
 #pragma unroll
         for (int j = 0; j < Sh::DMA_PER_TILE; ++j) dma16_to_lds_stream(kc + tile + koff[j], dst + j * 1024);
@@ -305,7 +311,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
         if (k == 0) load_q();
         if (appends && k == nbw - 1) {
             // the host appends here only when a partition has at most 64 blocks
-            const int pb = __builtin_amdgcn_readlane(ids, min(nblk - 1, 63));
+            const int pb = __builtin_amdgcn_readlane(ids, min((nblk - 1) / HALVES, 63));
             if (lane < NG) {
                 const u32x4 kg = *(const u32x4*)(new_lds + lane * 16);
                 const u32x4 vg = *(const u32x4*)(new_lds + ROWB + lane * 16);
@@ -313,20 +319,22 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
                 *(u32x4*)(row + ((lane ^ (new_row & (NG - 1))) * 16)) = kg;  // K granules are swizzled
                 *(u32x4*)(row + TILE + lane * 16) = vg;
                 if ((unsigned)pb < (unsigned)a.num_blocks) {
-                    const size_t dst = ((size_t)pb * a.num_kv_heads + kvh) * TILE + new_row * ROWB + lane * 16;
+                    const size_t dst = ((size_t)pb * a.num_kv_heads + kvh) * POOL_TILE + ((T - 1) % BS) * ROWB + lane * 16;
                     *(u32x4*)((char*)a.k_cache + dst) = kg;
                     *(u32x4*)((char*)a.v_cache + dst) = vg;
                 }
             }
         }
         const char* sp = ring + stage * Sh::STAGE;
-        const int blk_tok0 = (lb0 + kb0 + k) * BS;
-        if (blk_tok0 + BS <= T) {
+        const int blk_tok0 = (lb0 * HALVES + kb0 + k) * 16;
+        // one 16-row chunk per staged tile (kept as a loop: the same code as
+        // the chunk loop of a full block, which the compiler schedules best)
+        if (blk_tok0 + 16 <= T) {
 #pragma unroll
-            for (int ch = 0; ch < BS / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::false_type{});
+            for (int ch = 0; ch < 16 / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::false_type{});
         } else {
 #pragma unroll
-            for (int ch = 0; ch < BS / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::true_type{});
+            for (int ch = 0; ch < 16 / 16; ++ch) chunk(sp, ch, blk_tok0 + ch * 16, std::true_type{});
         }
         stage = stage + 1 == S ? 0 : stage + 1;
     }
@@ -382,7 +390,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
 
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
 int launch_partition_gqa4_as(const DecodeArgs& a, hipStream_t stream) {
-    using Sh = GqaShape<KV, D, BS, W, S>;
+    using Sh = GqaShape<KV, D, 16, W, S>;  // staged 16 rows at a time
     constexpr int LDS = APPEND ? Sh::LDS_APPEND : Sh::LDS;
     auto kernel = decode_partition_gqa4_kernel<KV, D, BS, W, S, APPEND>;
     static const hipError_t attr =

@@ -133,6 +133,7 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1023, 1024, 1025]
 
 @pytest.mark.parametrize("kv,q,heads,kv_heads,dim,block", [
     ("bf16", "bf16", 32, 8, 128, 16),
+    ("bf16", "bf16", 32, 8, 128, 32),   # GQA-4, 32-token blocks staged as two 16-row tiles
     ("bf16", "bf16", 8, 4, 64, 32),
     ("bf16", "bf16", 16, 2, 128, 32),
     ("bf16", "bf16", 16, 4, 64, 16),

@@ -310,12 +310,17 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     return PA_OK;
 }
 
+// the work order, when the partition workgroups do not compute it themselves
+static int run_plan(const Prepared& pr, hipStream_t stream) {
+    if (pr.args.max_partitions == 0 || pr.args.inline_plan) return PA_OK;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pr.args);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 static int run_partition(const Prepared& pr, hipStream_t stream) {
     if (pr.args.max_partitions == 0) return PA_OK;  // every sequence is empty
-    if (!pr.args.inline_plan) {
-        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, pr.args);
-        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-    }
+    const int sp = run_plan(pr, stream);
+    if (sp != PA_OK) return sp;
     switch (pr.kv_dtype) {
         case PA_DTYPE_F32: return launch_partition_f32(pr.args, pr.head_dim, pr.group, stream);
         case PA_DTYPE_F16: return launch_partition_f16(pr.args, pr.head_dim, pr.group, stream);
@@ -502,6 +507,18 @@ extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_st
     }
     int32_t* skip = (int32_t*)((char*)workspace + pa::skip_offset(num_seqs, num_heads, head_dim,
                                                                   pr.args.max_partitions));
+    if (pa::prefix_fused_supported(pr.kv_dtype, pr.q_dtype, pr.head_dim, block_size, pr.group)) {
+        // the skips, the work order, then the shared and the decode partitions in one launch
+        pr.args.skip_parts = skip;
+        int sf = pa::launch_prefix_skips(pr.args, group_start, group_prefix, num_groups, max_group_size,
+                                         max_prefix_len, skip, s);
+        if (sf == PA_OK) sf = pa::run_plan(pr, s);
+        if (sf == PA_OK)
+            sf = pa::launch_prefix_fused(pr.args, pr.kv_dtype, group_start, group_prefix, num_groups, max_group_size,
+                                         max_prefix_len, skip, s);
+        if (sf != PA_OK) return sf;
+        return pa::run_reduce(pr, s);
+    }
     const int s0 = pa::launch_prefix_states(pr.args, pr.kv_dtype, pr.group, group_start, group_prefix, num_groups,
                                             max_group_size, max_prefix_len, skip, s);
     if (s0 != PA_OK) return s0;

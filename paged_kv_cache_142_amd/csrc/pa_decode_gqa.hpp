@@ -96,9 +96,11 @@ constexpr int gqa_waves_per_simd() {
     return per_cu < 1 ? 1 : per_cu > PA_GQA_WAVES_PER_SIMD ? PA_GQA_WAVES_PER_SIMD : per_cu;
 }
 
+// The partition workgroup's work, for workgroup bid of the partition grid
+// (the kernel below passes its block index; the shared-prefix launch runs it
+// after its own workgroups).
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
-__global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
-decode_partition_gqa4_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid) {
     // Tiles are staged 16 rows at a time whatever the pool's block size BS:
     // a 32-token block is two 16-row halves, each a contiguous tile.
     using Sh = GqaShape<KV, D, 16, W, S>;
@@ -119,7 +121,7 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
     const int c = lane % NG;
 
     int seq, kvh, part;
-    if (!partition_work_item(a, seq, kvh, part)) return;
+    if (!partition_work_item(a, bid, seq, kvh, part)) return;
     const int P = a.partition_size;
     const int lb0 = part * P / BS;  // first logical block of the partition
     // Block ids of the whole partition, fetched together with the sequence
@@ -386,6 +388,12 @@ decode_partition_gqa4_kernel(const DecodeArgs a) {
             store_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     }
+}
+
+template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
+__global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
+decode_partition_gqa4_kernel(const DecodeArgs a) {
+    gqa4_partition<KV, D, BS, W, S, APPEND>(a, blockIdx.x);
 }
 
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>

@@ -153,18 +153,23 @@ __device__ __forceinline__ bool inline_plan_item(const DecodeArgs& a, int k, int
     return seq < a.num_seqs && part >= 0;
 }
 
-// The (sequence, kv head, partition) of this partition workgroup: workgroup
-// x = item * num_kv_heads + kv head, items in the plan's order.  Returns
-// false for workgroups past the last item.
-__device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, int& seq, int& kvh, int& part) {
-    const int item = blockIdx.x / a.num_kv_heads;
-    kvh = blockIdx.x - item * a.num_kv_heads;
+// The (sequence, kv head, partition) of partition workgroup bid (normally
+// the block index): bid = item * num_kv_heads + kv head, items in the plan's
+// order.  Returns false for workgroups past the last item.
+__device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, unsigned bid, int& seq, int& kvh,
+                                                    int& part) {
+    const int item = bid / a.num_kv_heads;
+    kvh = bid - item * a.num_kv_heads;
     if (a.inline_plan) return inline_plan_item(a, item, seq, part);
     if (item >= a.plan[0]) return false;
     const int code = a.plan[PLAN_ITEMS_OFFSET + item];
     seq = code / a.max_partitions;
     part = code - seq * a.max_partitions;
     return true;
+}
+
+__device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, int& seq, int& kvh, int& part) {
+    return partition_work_item(a, blockIdx.x, seq, kvh, part);
 }
 
 __device__ __forceinline__ void store_out(void* out, int dtype, size_t idx, float v) {
@@ -644,6 +649,13 @@ bool prefix_states_supported(int kv_dtype, int q_dtype, int head_dim, int block_
 int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int32_t* group_start,
                          const int32_t* group_prefix, int num_groups, int max_group_size, int max_prefix_len,
                          int32_t* skip, hipStream_t stream);
+// 4-head groups: the skips first (a small kernel), then, after the plan if
+// any, one launch for the shared partitions and the decode partitions.
+bool prefix_fused_supported(int kv_dtype, int q_dtype, int head_dim, int block_size, int group);
+int launch_prefix_skips(const DecodeArgs& d, const int32_t* group_start, const int32_t* group_prefix,
+                        int num_groups, int max_group_size, int max_prefix_len, int32_t* skip, hipStream_t stream);
+int launch_prefix_fused(const DecodeArgs& d, int kv_dtype, const int32_t* group_start, const int32_t* group_prefix,
+                        int num_groups, int max_group_size, int max_prefix_len, int32_t* skip, hipStream_t stream);
 
 // Per-format dispatch over head_dim, block_size and group size; defined in
 // one translation unit per KV format.

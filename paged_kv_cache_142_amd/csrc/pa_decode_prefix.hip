@@ -15,10 +15,17 @@
 // partition kernel then skips those partitions (skip_parts) and the reduce
 // kernel merges all of a sequence's partitions as usual.
 //
+// For 4-head groups the shared partitions and the decode partitions run in
+// one launch (shared_prefix_fused_kernel): its first workgroups compute the
+// shared partitions, the rest are the GQA-4 partition kernel's workgroups.
+// Both kinds are short and would each leave the device partly idle.  The
+// skips are then written by a small kernel before that launch.
+//
 // A member that holds fewer tokens than the shared partitions (or whose
 // length is invalid) is not shared: its skip is 0 and the decode kernels
 // compute it alone.  A leader shorter than the shared partitions disables
 // sharing for its group.
+#include "pa_decode_gqa.hpp"
 #include "pa_mq_mfma.hpp"
 
 #ifndef PA_PREFIX_STAGES
@@ -35,11 +42,74 @@ struct PrefixArgs {
     int num_groups;
     int chunks;                   // member chunks per group in the grid
     int parts;                    // shared partitions per group in the grid
-    int32_t* skip;                // [num_seqs] written here, read by the decode plan
+    int member_cap;               // members per group the grid covers (chunks * columns per workgroup)
+    bool write_skips;             // the states' workgroups write the skips (else prefix_skip_kernel does)
+    int32_t* skip;                // [num_seqs] read by the decode plan
 };
 
+// The members of group grp and the number of shared partitions the group's
+// workgroups compute (0: none).  The skips and the states are both decided
+// from this, so they match.
+struct GroupShare {
+    int s0, s1;       // members [s0, s1)
+    bool members_ok;  // the range lies inside the batch
+    int nparts;
+};
+
+template <int BS>
+__device__ inline bool length_ok(const DecodeArgs& d, int T) {
+    return T > 0 && T <= d.max_seq_len && (T + BS - 1) / BS <= d.max_blocks_per_seq;
+}
+
+template <int BS>
+__device__ inline GroupShare group_share(const PrefixArgs& a, int grp) {
+    const DecodeArgs& d = a.d;
+    const int P = d.partition_size;
+    GroupShare gs;
+    gs.s0 = a.group_start[grp];
+    gs.s1 = a.group_start[grp + 1];
+    gs.members_ok = 0 <= gs.s0 && gs.s0 <= gs.s1 && gs.s1 <= d.num_seqs;
+    gs.nparts = 0;
+    if (gs.members_ok && gs.s1 > gs.s0) {
+        const int pre = a.group_prefix[grp];
+        const int T0 = d.seq_lens[gs.s0];
+        gs.nparts = pre > 0 ? min(pre / P, a.parts) : 0;  // never more than the grid covers
+        if (!length_ok<BS>(d, T0) || T0 < gs.nparts * P) gs.nparts = 0;  // the leader must hold them
+    }
+    return gs;
+}
+
+// whether a member of length T shares the group's partitions
+template <int BS>
+__device__ inline bool member_shares(const PrefixArgs& a, const GroupShare& gs, int T) {
+    return gs.nparts > 0 && length_ok<BS>(a.d, T) && T >= gs.nparts * a.d.partition_size;
+}
+
+// The skips of group grp's members, and of the sequences before the first
+// group and after the last one, which no group covers (256 threads).
+// Members past the grid's chunks are computed alone.
+template <int BS>
+__device__ inline void write_group_skips(const PrefixArgs& a, int grp, const GroupShare& gs) {
+    const int n = a.d.num_seqs;
+    if (gs.members_ok)
+        for (int i = gs.s0 + (int)threadIdx.x; i < gs.s1; i += 256)
+            a.skip[i] = (i - gs.s0 < a.member_cap && member_shares<BS>(a, gs, a.d.seq_lens[i])) ? gs.nparts : 0;
+    if (grp == 0)
+        for (int i = threadIdx.x; i < min(max(gs.s0, 0), n); i += 256) a.skip[i] = 0;
+    if (grp == a.num_groups - 1)
+        for (int i = max(gs.s1, 0) + (int)threadIdx.x; i < n; i += 256) a.skip[i] = 0;
+}
+
+// one workgroup per group
+template <int BS>
+__global__ void __launch_bounds__(256) prefix_skip_kernel(const PrefixArgs a) {
+    const GroupShare gs = group_share<BS>(a, blockIdx.x);
+    write_group_skips<BS>(a, blockIdx.x, gs);
+}
+
+// The work of workgroup bid of the shared partitions' grid.
 template <Fmt KV, int D, int BS, int G>
-__global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs a) {
+__device__ __forceinline__ void prefix_states(const PrefixArgs& a, unsigned bid) {
     using Sh = MqShape<D, BS, G, 1, PA_PREFIX_STAGES>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const DecodeArgs& d = a.d;
@@ -51,7 +121,7 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
     const int H = d.num_kv_heads;
     const int P = d.partition_size;
 
-    int rest = blockIdx.x;
+    int rest = (int)bid;
     const int kvh = rest % H;
     rest /= H;
     const int chunk = rest % a.chunks;
@@ -59,33 +129,10 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
     const int part = rest % a.parts;
     const int grp = rest / a.parts;
 
-    const int s0 = a.group_start[grp];
-    const int s1 = a.group_start[grp + 1];
-    auto length_ok = [&](int T) {
-        return T > 0 && T <= d.max_seq_len && (T + BS - 1) / BS <= d.max_blocks_per_seq;
-    };
-    const bool members_ok = 0 <= s0 && s0 <= s1 && s1 <= d.num_seqs;
-    int nparts = 0;  // shared partitions of the group
-    if (members_ok && s1 > s0) {
-        const int pre = a.group_prefix[grp];
-        const int T0 = d.seq_lens[s0];
-        nparts = pre > 0 ? min(pre / P, a.parts) : 0;  // never more than the grid covers
-        if (!length_ok(T0) || T0 < nparts * P) nparts = 0;  // the leader must hold the shared partitions
-    }
-    auto shares = [&](int T) { return nparts > 0 && length_ok(T) && T >= nparts * P; };
-
-    // the skips of the group's members (and of the sequences before the
-    // first group and after the last one, which no group covers)
-    if (part == 0 && chunk == 0 && kvh == 0) {
-        if (members_ok)
-            for (int i = s0 + (int)threadIdx.x; i < s1; i += 256)  // members past the grid's chunks: alone
-                a.skip[i] = (i - s0 < a.chunks * Sh::TQ && shares(d.seq_lens[i])) ? nparts : 0;
-        if (grp == 0)
-            for (int i = threadIdx.x; i < min(max(s0, 0), d.num_seqs); i += 256) a.skip[i] = 0;
-        if (grp == a.num_groups - 1)
-            for (int i = max(s1, 0) + (int)threadIdx.x; i < d.num_seqs; i += 256) a.skip[i] = 0;
-    }
-    if (!members_ok || part >= nparts) return;
+    const GroupShare gs = group_share<BS>(a, grp);
+    const int s0 = gs.s0, s1 = gs.s1, nparts = gs.nparts;
+    if (a.write_skips && part == 0 && chunk == 0 && kvh == 0) write_group_skips<BS>(a, grp, gs);
+    if (!gs.members_ok || part >= nparts) return;
     const int members = s1 - s0;
     const int mem_lo = chunk * Sh::TQ;
     if (mem_lo >= members) return;
@@ -101,7 +148,7 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
     t.key_end = (part + 1) * P;
     t.kv_len = t.key_end;
     t.kvh = kvh;
-    t.cvalid[0] = mi < members && shares(T);
+    t.cvalid[0] = mi < members && member_shares<BS>(a, gs, T);
     t.cpos[0] = t.key_end - 1;
     t.qptr[0] = (const char*)d.q + (((size_t)seq * d.num_heads + head) * D + 32 * g) * 2;
     t.wave_cols = mem_lo + wave * Sh::PER_WAVE < members;
@@ -142,17 +189,45 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
 }
 
 template <Fmt KV, int D, int BS, int G>
+__global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs a) {
+    prefix_states<KV, D, BS, G>(a, blockIdx.x);
+}
+
+// The shared partitions (workgroups below prefix_grid) and the decode
+// partitions of a 4-head-group batch in one launch.
+template <Fmt KV, int BS, bool APPEND>
+__global__ void __launch_bounds__(256, 2) shared_prefix_fused_kernel(const PrefixArgs a, unsigned prefix_grid) {
+    if (blockIdx.x < prefix_grid)
+        prefix_states<KV, 128, BS, 4>(a, blockIdx.x);
+    else
+        gqa4_partition<KV, 128, BS, 4, PA_GQA_STAGES, APPEND>(a.d, blockIdx.x - prefix_grid);
+}
+static_assert(PA_GQA_WAVES == 4, "the combined launch runs both kinds of workgroup with 256 threads");
+
+// Grid sizes for groups of G heads: member chunks and shared partitions per
+// group.  Returns the number of shared-partition workgroups, or -1 when it
+// does not fit a grid.
+template <int D, int BS, int G>
+static long long size_prefix_grid(PrefixArgs& a, int max_group_size, int max_prefix_len) {
+    using Sh = MqShape<D, BS, G, 1, PA_PREFIX_STAGES>;
+    a.chunks = max((max_group_size + Sh::TQ - 1) / Sh::TQ, 1);
+    a.parts = max(max_prefix_len / a.d.partition_size, 1);  // at least one: part 0 writes the skips
+    a.member_cap = a.chunks * Sh::TQ;
+    const long long grid = (long long)a.num_groups * a.chunks * a.parts * a.d.num_kv_heads;
+    return grid > 0x7fffffffLL ? -1 : grid;
+}
+
+template <Fmt KV, int D, int BS, int G>
 static int launch_prefix(PrefixArgs& a, int max_group_size, int max_prefix_len, hipStream_t stream) {
     using Sh = MqShape<D, BS, G, 1, PA_PREFIX_STAGES>;
     auto kernel = prefix_states_kernel<KV, D, BS, G>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    a.chunks = max((max_group_size + Sh::TQ - 1) / Sh::TQ, 1);
-    a.parts = max(max_prefix_len / a.d.partition_size, 1);  // at least one: the skips are written by part 0
-    const long long grid = (long long)a.num_groups * a.chunks * a.parts * a.d.num_kv_heads;
-    if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+    const long long grid = size_prefix_grid<D, BS, G>(a, max_group_size, max_prefix_len);
+    if (grid < 0) return PA_ERR_SHAPE;
     if (grid == 0) return PA_OK;
+    a.write_skips = true;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -175,9 +250,8 @@ bool prefix_states_supported(int kv_dtype, int q_dtype, int head_dim, int block_
            (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int32_t* group_start,
-                         const int32_t* group_prefix, int num_groups, int max_group_size, int max_prefix_len,
-                         int32_t* skip, hipStream_t stream) {
+static PrefixArgs make_prefix_args(const DecodeArgs& d, const int32_t* group_start, const int32_t* group_prefix,
+                                   int num_groups, int32_t* skip) {
     PrefixArgs a;
     a.d = d;
     a.pool.k_cache = d.k_cache;
@@ -188,12 +262,86 @@ int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int
     a.group_start = group_start;
     a.group_prefix = group_prefix;
     a.num_groups = num_groups;
+    a.write_skips = false;
     a.skip = skip;
+    return a;
+}
+
+int launch_prefix_states(const DecodeArgs& d, int kv_dtype, int group, const int32_t* group_start,
+                         const int32_t* group_prefix, int num_groups, int max_group_size, int max_prefix_len,
+                         int32_t* skip, hipStream_t stream) {
+    PrefixArgs a = make_prefix_args(d, group_start, group_prefix, num_groups, skip);
     if (kv_dtype == PA_DTYPE_BF16)
         return d.block_size == 16 ? dispatch_prefix_group<Fmt::BF16, 16>(a, group, max_group_size, max_prefix_len, stream)
                                   : dispatch_prefix_group<Fmt::BF16, 32>(a, group, max_group_size, max_prefix_len, stream);
     return d.block_size == 16 ? dispatch_prefix_group<Fmt::F16, 16>(a, group, max_group_size, max_prefix_len, stream)
                               : dispatch_prefix_group<Fmt::F16, 32>(a, group, max_group_size, max_prefix_len, stream);
 }
+
+#ifndef PA_DISABLE_GQA4
+bool prefix_fused_supported(int kv_dtype, int q_dtype, int head_dim, int block_size, int group) {
+    return prefix_states_supported(kv_dtype, q_dtype, head_dim, block_size, group) && group == 4;
+}
+
+template <int BS>
+static int launch_skips_for(PrefixArgs& a, int max_group_size, int max_prefix_len, hipStream_t stream) {
+    if (size_prefix_grid<128, BS, 4>(a, max_group_size, max_prefix_len) < 0) return PA_ERR_SHAPE;
+    if (a.num_groups == 0) return PA_OK;
+    hipLaunchKernelGGL(prefix_skip_kernel<BS>, dim3((unsigned)a.num_groups), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_prefix_skips(const DecodeArgs& d, const int32_t* group_start, const int32_t* group_prefix,
+                        int num_groups, int max_group_size, int max_prefix_len, int32_t* skip, hipStream_t stream) {
+    PrefixArgs a = make_prefix_args(d, group_start, group_prefix, num_groups, skip);
+    return d.block_size == 16 ? launch_skips_for<16>(a, max_group_size, max_prefix_len, stream)
+                              : launch_skips_for<32>(a, max_group_size, max_prefix_len, stream);
+}
+
+template <Fmt KV, int BS, bool APPEND>
+static int launch_fused_as(PrefixArgs& a, int max_group_size, int max_prefix_len, hipStream_t stream) {
+    using Sp = MqShape<128, BS, 4, 1, PA_PREFIX_STAGES>;
+    using Sg = GqaShape<KV, 128, 16, 4, PA_GQA_STAGES>;
+    constexpr int LDS_G = APPEND ? Sg::LDS_APPEND : Sg::LDS;
+    constexpr int LDS = Sp::LDS > LDS_G ? Sp::LDS : LDS_G;
+    auto kernel = shared_prefix_fused_kernel<KV, BS, APPEND>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess) return PA_ERR_LAUNCH;
+    const long long prefix_grid = size_prefix_grid<128, BS, 4>(a, max_group_size, max_prefix_len);
+    if (prefix_grid < 0) return PA_ERR_SHAPE;
+    const long long grid =
+        (a.num_groups > 0 ? prefix_grid : 0) + (long long)a.d.num_seqs * a.d.max_partitions * a.d.num_kv_heads;
+    if (grid > 0x7fffffffLL) return PA_ERR_SHAPE;
+    if (grid == 0) return PA_OK;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), LDS, stream, a,
+                       (unsigned)(a.num_groups > 0 ? prefix_grid : 0));
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <Fmt KV, int BS>
+static int launch_fused_for(PrefixArgs& a, int mgs, int mpl, hipStream_t s) {
+    return a.d.new_k != nullptr ? launch_fused_as<KV, BS, true>(a, mgs, mpl, s)
+                                : launch_fused_as<KV, BS, false>(a, mgs, mpl, s);
+}
+
+int launch_prefix_fused(const DecodeArgs& d, int kv_dtype, const int32_t* group_start, const int32_t* group_prefix,
+                        int num_groups, int max_group_size, int max_prefix_len, int32_t* skip, hipStream_t stream) {
+    PrefixArgs a = make_prefix_args(d, group_start, group_prefix, num_groups, skip);
+    if (kv_dtype == PA_DTYPE_BF16)
+        return d.block_size == 16 ? launch_fused_for<Fmt::BF16, 16>(a, max_group_size, max_prefix_len, stream)
+                                  : launch_fused_for<Fmt::BF16, 32>(a, max_group_size, max_prefix_len, stream);
+    return d.block_size == 16 ? launch_fused_for<Fmt::F16, 16>(a, max_group_size, max_prefix_len, stream)
+                              : launch_fused_for<Fmt::F16, 32>(a, max_group_size, max_prefix_len, stream);
+}
+#else
+bool prefix_fused_supported(int, int, int, int, int) { return false; }
+int launch_prefix_skips(const DecodeArgs&, const int32_t*, const int32_t*, int, int, int, int32_t*, hipStream_t) {
+    return PA_ERR_UNSUPPORTED;
+}
+int launch_prefix_fused(const DecodeArgs&, int, const int32_t*, const int32_t*, int, int, int, int32_t*, hipStream_t) {
+    return PA_ERR_UNSUPPORTED;
+}
+#endif
 
 }  // namespace pa

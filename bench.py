@@ -65,8 +65,9 @@ def _parse():
     p.add_argument("--partition-size", type=int, default=None,
                    help="split-KV partition size (default: the fastest in same-box sweeps where the workload "
                         "leaves it open: 768 for gqa (512..1024 tried), 256 for shared_prefix_grouped and "
-                        "shared_prefix_cow_grouped (128..512 tried); 512 for the other workloads, the pages' "
-                        "value for the long-context case)")
+                        "shared_prefix_cow_grouped (128..512 tried), 1024 for shared_prefix_long_grouped "
+                        "(256..1024 tried); 512 for the other workloads, the pages' value for the long-context "
+                        "case)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
     p.add_argument("--pools", type=int, default=2,
@@ -279,7 +280,8 @@ def run_prefill(args):
 def _workload(name, seed, partition_size):
     import workloads
     if partition_size is None:
-        partition_size = {"gqa": 768, "shared_prefix_grouped": 256, "shared_prefix_cow_grouped": 256}.get(name, 512)
+        partition_size = {"gqa": 768, "shared_prefix_grouped": 256, "shared_prefix_cow_grouped": 256,
+                          "shared_prefix_long_grouped": 1024}.get(name, 512)
     if name.startswith("shared_prefix_cow"):
         return shared_prefix_step(seed, partition_size, 1032)
     if name.startswith("shared_prefix_long"):

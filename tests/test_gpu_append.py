@@ -125,6 +125,7 @@ def test_append_invalid_last_block_stores_nothing(heads, kv_heads):
     (32, 8, "bf16", 16, 256),   # G = 4: the suffix partitions' kernel stores the token
     (16, 16, "bf16", 16, 256),  # G = 1: copy kernel first
     (32, 4, "f16", 32, 512),    # G = 8
+    (32, 8, "bf16", 16, 1024),  # 64 blocks per partition: the most the partition kernel stores the token for
 ])
 def test_shared_prefix_decode_with_append(heads, kv_heads, fmt, block, P):
     """pa_decode_shared_prefix given each sequence's newest token: the pools

@@ -194,7 +194,12 @@ __global__ void __launch_bounds__(256, 2) prefix_states_kernel(const PrefixArgs 
 }
 
 // The shared partitions (workgroups below prefix_grid) and the decode
-// partitions of a 4-head-group batch in one launch.
+// partitions of a 4-head-group batch in one launch.  The two kinds run
+// concurrently and share no data: the first write the partition slots below
+// each member's skip (or a one-partition member's output row) and read only
+// blocks of the shared partitions; the others write the slots from the skip on
+// and, with APPEND, store each sequence's newest token, which lies past its
+// group's shared tokens and so in a block the first kind does not read.
 template <Fmt KV, int BS, bool APPEND>
 __global__ void __launch_bounds__(256, 2) shared_prefix_fused_kernel(const PrefixArgs a, unsigned prefix_grid) {
     if (blockIdx.x < prefix_grid)

@@ -123,8 +123,12 @@ def quantize_reshape_and_cache(k_cache, v_cache, key32, value32, k_scale, v_scal
     "KVキャッシュとPagedAttention — 推論メモリのすべて", section "KV量子化:
     FP8とINT8".
 
-    Parity: the encoder is pinned in the oracle tests; the scatter is the
-    pinned ``reshape_and_cache``.
+    Parity: the whole call is pinned against a reference built from torch
+    alone (float32 division by each head's own K or V scale, clamp to +-448,
+    torch's float8_e4m3fn rounding, scatter by advanced indexing), on inputs
+    chosen so that a float64 division, a neighbouring head's scale or the
+    other tensor's scale each change a stored code; the encoder is also
+    pinned on its own.
     """
     from .formats import quantize_to_e4m3fn
     key32 = np.asarray(key32, dtype=np.float32)

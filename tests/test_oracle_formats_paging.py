@@ -235,3 +235,134 @@ def test_quantize_uses_float32_division():
     want = formats.e4m3fn_encode((x / s).astype(np.float64))
     assert np.array_equal(formats.quantize_to_e4m3fn(x, s), want)
     assert formats.e4m3fn_table()[formats.quantize_to_e4m3fn(np.array([448 * 0.1], np.float32), s)[0]] == 448.0
+
+
+# ------------------------------------------- quantize-on-write, pinned to torch
+#
+# FP8 KV storage keeps a scale beside the 8-bit codes (youngju.dev,
+# "KVキャッシュとPagedAttention — 推論メモリのすべて", section "KV量子化: FP8と
+# INT8").  The reference below is built from torch alone: the IEEE float32
+# quotient of each element by its own kv head's scale (K and V scales apart),
+# clamped to the format's range (torch turns out-of-range values into NaN
+# rather than saturating), converted by torch's float8_e4m3fn rounding, and
+# scattered by advanced indexing.  It shares no step with the oracle.
+
+
+def _e4m3_neighbours():
+    """Pairs (lo, hi, code_lo, code_hi) of neighbouring positive finite
+    E4M3FN values, from torch's decoding of the codes."""
+    codes = torch.arange(0x00, 0x7F, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return [(vals[c], vals[c + 1], c, c + 1) for c in range(len(vals) - 1)]
+
+
+def _division_sensitive_inputs(scales):
+    """float32 x per scale s whose E4M3 code differs between the float32
+    quotient x/s (the stated reading) and the exact quotient.
+
+    Each x is a float32 neighbour of mid * s, mid halfway between two codes.
+    The float32 quotient (torch's IEEE division) and the exact quotient
+    (float64 division, exact to well below a float32 ulp here) are compared
+    with mid in float64: they pick different codes when they fall on
+    opposite sides of it, or when the float32 one lands on it exactly (ties
+    go to the even code) and the exact one lies on the odd code's side.
+    torch's own float64 -> float8 conversion rounds through float32, so it
+    cannot stand in for the exact side.
+    """
+    picked = {}
+    for h, s in enumerate(scales):
+        xs = []
+        for lo, hi, c_lo, _ in _e4m3_neighbours()[::5]:
+            mid = (lo + hi) / 2
+            x0 = np.float32(mid * np.float64(s))
+            for k in range(-3, 4):
+                x = x0
+                for _ in range(abs(k)):
+                    x = np.nextafter(x, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+                q32 = float((torch.tensor([x]) / torch.tensor([s])).item())
+                q64 = float(np.float64(x) / np.float64(s))
+                side32 = np.sign(q32 - mid)
+                side64 = np.sign(q64 - mid)
+                odd_side = -1.0 if c_lo % 2 else 1.0
+                if (side32 * side64 < 0) or (side32 == 0 and side64 == odd_side):
+                    xs.append(x)
+        picked[h] = np.array(xs, np.float32)
+    return picked
+
+
+def _torch_quantized_pool(pool_shape, key32, value32, k_scale, v_scale, slots, block_size):
+    kx = torch.from_numpy(key32)
+    vx = torch.from_numpy(value32)
+    ks = torch.from_numpy(k_scale)[None, :, None]
+    vs = torch.from_numpy(v_scale)[None, :, None]
+    kc = (kx / ks).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc = (vx / vs).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    kp = torch.full(pool_shape, 0xA5, dtype=torch.uint8)
+    vp = torch.full(pool_shape, 0xA5, dtype=torch.uint8)
+    s = torch.from_numpy(slots)
+    keep = s >= 0
+    blk, row = s[keep] // block_size, s[keep] % block_size
+    kp[blk, :, row, :] = kc[keep]
+    vp[blk, :, row, :] = vc[keep]
+    return kp.numpy(), vp.numpy()
+
+
+def _quantize_case(seed=23):
+    rng = np.random.default_rng(seed)
+    num_tokens, hkv, d, bs, nb = 24, 4, 64, 16, 5
+    k_scale = np.array([0.1, 0.3, 0.07, 1 / 3], np.float32)
+    v_scale = np.array([0.013, 0.9, 0.41, 0.05], np.float32)
+    key32 = (rng.standard_normal((num_tokens, hkv, d)) * 4).astype(np.float32)
+    value32 = (rng.standard_normal((num_tokens, hkv, d)) * 4).astype(np.float32)
+    # plant the division-sensitive values of each head's own scale, and
+    # out-of-range values that must saturate
+    for arr, scales in ((key32, k_scale), (value32, v_scale)):
+        for h, xs in _division_sensitive_inputs(scales).items():
+            flat = arr[:, h, :].reshape(-1)
+            idx = rng.choice(flat.size, size=len(xs), replace=False)
+            flat[idx] = xs * rng.choice([-1, 1], size=len(xs))
+            arr[:, h, :] = flat.reshape(num_tokens, d)
+        arr[0, :, 0] = 1e6
+        arr[1, :, 1] = -np.inf
+    slots = rng.permutation(nb * bs)[:num_tokens].astype(np.int64)
+    slots[5] = -1  # a skipped token
+    return key32, value32, k_scale, v_scale, slots, bs, (nb, hkv, bs, d)
+
+
+def test_quantize_reshape_and_cache_matches_torch_per_head():
+    key32, value32, k_scale, v_scale, slots, bs, shape = _quantize_case()
+    kp = np.full(shape, 0xA5, np.uint8)
+    vp = np.full(shape, 0xA5, np.uint8)
+    oracle.quantize_reshape_and_cache(kp, vp, key32, value32, k_scale, v_scale, slots, bs)
+    want_k, want_v = _torch_quantized_pool(shape, key32, value32, k_scale, v_scale, slots, bs)
+    assert np.array_equal(kp, want_k)
+    assert np.array_equal(vp, want_v)
+
+
+def test_quantize_pin_discriminates_plausible_oracle_mistakes(monkeypatch):
+    """The inputs above separate the stated reading from its near misses.
+    Each mistake is planted in the oracle (on the CPU) and must change at
+    least one stored code: dividing in float64, taking a neighbouring head's
+    scale, or taking the V scale for K."""
+    key32, value32, k_scale, v_scale, slots, bs, shape = _quantize_case()
+    for h, xs in _division_sensitive_inputs(k_scale).items():
+        assert len(xs) >= 3, f"too few division-sensitive values for head {h}"
+    want_k, want_v = _torch_quantized_pool(shape, key32, value32, k_scale, v_scale, slots, bs)
+
+    def run(ks, vs):
+        kp = np.full(shape, 0xA5, np.uint8)
+        vp = np.full(shape, 0xA5, np.uint8)
+        oracle.quantize_reshape_and_cache(kp, vp, key32, value32, ks, vs, slots, bs)
+        return kp, vp
+
+    kp, vp = run(k_scale, v_scale)
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v)
+    for ks, vs in ((np.roll(k_scale, 1), v_scale), (v_scale, v_scale), (k_scale, np.roll(v_scale, -1))):
+        kp, vp = run(ks, vs)
+        assert not (np.array_equal(kp, want_k) and np.array_equal(vp, want_v))
+    with monkeypatch.context() as m:
+        m.setattr(formats, "quantize_to_e4m3fn",
+                  lambda x, s: formats.e4m3fn_encode(np.asarray(x, np.float64) / np.float64(s)))
+        kp, vp = run(k_scale, v_scale)
+    assert not np.array_equal(kp, want_k)
+    assert not np.array_equal(vp, want_v)

@@ -79,7 +79,8 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = -5,   /* workspace smaller than pa_decode_workspace_size()   */
     PA_ERR_LAUNCH = -6,      /* the HIP runtime rejected a kernel launch           */
     PA_ERR_MEMORY = -7,      /* a pool the GPU cannot address (pa_swap_blocks)      */
-    PA_ERR_CONTENT = -8      /* checked build only: device contents break the contract */
+    PA_ERR_CONTENT = -8,     /* checked build only: device contents break the contract */
+    PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: the call needs more than its static scratch */
 } pa_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -257,6 +258,33 @@ int pa_decode(void* out, int out_dtype, const void* q, int q_dtype, const void* 
               int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
               float scale, const float* k_scale, const float* v_scale, int partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and results as pa_decode,
+ * with the split-KV workspace taken from a static device array of the
+ * library instead of a caller's buffer.
+ *
+ * Arguments: those of pa_decode without workspace and workspace_bytes.
+ * The library's static array holds PA_DECODE_NOALLOC_SCRATCH_BYTES bytes on
+ * every GPU it runs on, from the first call on that GPU until the process
+ * ends; the call looks up its device address once per device and then
+ * calls no allocating routine.  A call whose pa_decode_workspace_size(...)
+ * exceeds that size returns PA_ERR_SCRATCH before touching the device.
+ * Every call on one GPU shares that GPU's array, whose contents on entry do
+ * not matter: calls that overlap in time on one GPU (two streams, or two
+ * host threads) race on it and give undefined results; calls ordered on one
+ * stream are safe.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int pa_decode_noalloc(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                      const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                      float scale, const float* k_scale, const float* v_scale, int partition_size,
+                      void* stream);
 
 /*
  * pa_decode_partition, pa_decode_reduce -- the two launches of pa_decode,

@@ -204,6 +204,16 @@ def pa_decode(*args, **kw):
     _decode_call("pa_decode", *args, **kw)
 
 
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, partition_size,
+                      k_scale=None, v_scale=None, kv_dtype=None, q_dtype=None, out_dtype=None, stream=None):
+    """``pa_decode`` with the split-KV workspace in the library's static
+    device array (no workspace argument; the call allocates nothing)."""
+    argv = _decode_argv(out, q, k_cache, v_cache, block_tables, seq_lens, max_seq_len, scale, partition_size,
+                        None, k_scale=k_scale, v_scale=v_scale, kv_dtype=kv_dtype, q_dtype=q_dtype,
+                        out_dtype=out_dtype, stream=stream)
+    _check(_lib.load().pa_decode_noalloc(*argv[:21], argv[23]), "pa_decode_noalloc")
+
+
 def _append_argv(key, value, args, kw):
     q = kw["q"] if "q" in kw else args[1]
     k_cache = kw["k_cache"] if "k_cache" in kw else args[2]

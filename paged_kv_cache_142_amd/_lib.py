@@ -33,6 +33,7 @@ SIGNATURES = {
     "pa_prefill": (_c_int, [_vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _c_int, _vp,
                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp]),
     "pa_decode": (_c_int, _DECODE_ARGS),
+    "pa_decode_noalloc": (_c_int, _DECODE_ARGS[:21] + [_vp]),
     "pa_decode_partition": (_c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c_int, _DECODE_ARGS),
     "pa_decode_append": (_c_int, _DECODE_ARGS + [_vp, _vp]),

@@ -147,6 +147,7 @@ extern "C" const char* pa_status_string(int status) {
         case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
         case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pool is neither device memory nor pinned host memory the device can address";
         case PA_ERR_CONTENT: return "PA_ERR_CONTENT: device contents break the call's contract (checked build)";
+        case PA_ERR_SCRATCH: return "PA_ERR_SCRATCH: pa_decode_noalloc needs more workspace than its static scratch holds";
         default: return "unknown pa_status";
     }
 }

@@ -3,6 +3,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_decode_kernel.hpp"
 
 namespace pa {
@@ -225,6 +227,15 @@ static void launch_reduce_for(const DecodeArgs& a, hipStream_t stream) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Point the partition states and the plan into a workspace laid out as
+// workspace_bytes_for describes (rows = N * H * P_max state rows).
+static void bind_workspace(DecodeArgs& a, void* workspace, size_t rows, size_t plan_at) {
+    a.part_m = (float*)workspace;
+    a.part_l = (float*)((char*)workspace + align256(rows * 4));
+    a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
+    a.plan = (int*)((char*)workspace + plan_at);
+}
+
 struct Prepared {
     DecodeArgs args;
     int head_dim;
@@ -240,7 +251,7 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
                    int max_seq_len, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                    int block_size, int num_blocks, float scale, const float* k_scale,
                    const float* v_scale, int partition_size, void* workspace,
-                   size_t workspace_bytes) {
+                   size_t workspace_bytes, bool bind_later = false) {
     const bool combo_ok = (kv_dtype == PA_DTYPE_F32 && q_dtype == PA_DTYPE_F32) ||
                           (kv_dtype == PA_DTYPE_F16 && q_dtype == PA_DTYPE_F16) ||
                           (kv_dtype == PA_DTYPE_BF16 && q_dtype == PA_DTYPE_BF16) ||
@@ -270,9 +281,11 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     if (kv_dtype == PA_DTYPE_FP8_E4M3 && (!k_scale || !v_scale)) return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
     const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, max_parts);
-    if (need > 0 && !workspace) return PA_ERR_NULL;
-    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(workspace)) return PA_ERR_SHAPE;
+    if (!bind_later) {
+        if (need > 0 && !workspace) return PA_ERR_NULL;
+        if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+        if (need > 0 && !aligned16(workspace)) return PA_ERR_SHAPE;
+    }
 
     const size_t rows = (size_t)num_seqs * num_heads * max_parts;
     DecodeArgs& a = pr.args;
@@ -295,10 +308,7 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.v_scale = v_scale;
     a.partition_size = partition_size;
     a.max_partitions = max_parts;
-    a.part_m = (float*)workspace;
-    a.part_l = (float*)((char*)workspace + align256(rows * 4));
-    a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
-    a.plan = (int*)((char*)workspace + plan_offset(num_seqs, num_heads, head_dim, max_parts));
+    bind_workspace(a, workspace, rows, plan_offset(num_seqs, num_heads, head_dim, max_parts));
     a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
     a.skip_parts = nullptr;
     a.new_k = nullptr;
@@ -526,4 +536,75 @@ extern "C" int pa_decode_shared_prefix(PA_DECODE_PARAMS, const int32_t* group_st
     const int s1 = pa::run_partition(pr, s);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, s);
+}
+
+// ------------------------------------------------------------ pa_decode_noalloc
+//
+// pa_decode with its workspace in a static device array instead of the
+// caller's buffer, for callers that cannot allocate.  The array is a
+// file-scope __device__ variable: every GPU the library runs on holds its own
+// copy (PA_DECODE_NOALLOC_SCRATCH_BYTES) until the process ends.  Host code
+// never uses the variable's name as an address (on the host it is only a
+// stand-in); its device address is looked up once per device with that device
+// current and kept in scratch_ptr.
+
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace pa {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// Device address of `scratch` on the device that runs `stream`.
+static int scratch_for_stream(hipStream_t stream, void** out) {
+    int current = 0;
+    if (hipGetDevice(&current) != hipSuccess) return PA_ERR_LAUNCH;
+    int dev = current;
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return PA_ERR_LAUNCH;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return PA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != current && hipSetDevice(dev) != hipSuccess) return PA_ERR_LAUNCH;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != current) (void)hipSetDevice(current);
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return PA_ERR_LAUNCH;
+        }
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" int pa_decode_noalloc(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                                 const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                                 int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                                 int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 float scale, const float* k_scale, const float* v_scale, int partition_size,
+                                 void* stream) {
+    // every argument is checked before the device is touched
+    void* workspace = nullptr;
+    const size_t workspace_bytes = PA_DECODE_NOALLOC_SCRATCH_BYTES;
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS, /*bind_later=*/true);
+    if (st != PA_OK || pr.nothing_to_do) return st;
+    const int mp = pr.args.max_partitions;
+    if (pa::workspace_bytes_for(num_seqs, num_heads, head_dim, mp) > workspace_bytes) return PA_ERR_SCRATCH;
+    const int sp = pa::scratch_for_stream((hipStream_t)stream, &workspace);
+    if (sp != PA_OK) return sp;
+    pa::bind_workspace(pr.args, workspace, (size_t)num_seqs * num_heads * mp,
+                       pa::plan_offset(num_seqs, num_heads, head_dim, mp));
+    PA_CHECK_SEQUENCES();
+    const int s1 = pa::run_partition(pr, (hipStream_t)stream);
+    if (s1 != PA_OK) return s1;
+    return pa::run_reduce(pr, (hipStream_t)stream);
 }

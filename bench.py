@@ -15,10 +15,13 @@ effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
 By default two copies of the K/V pool alternate between steps, so that no
 step finds the previous step's K/V in the 256 MB Infinity Cache (on MI355X
 this costs about 1% against re-reading one pool; ``--pools 1`` for that).
-Also reported: ``pa_decode`` alone, called back to back (``decode_alone_*``),
-and per-call durations from a second loop with HIP events around each of
-the separate launches (scatter, copies, partition, reduce: ``kernels_us``),
-from which the roofline of the partition launch is taken.
+
+Timing: ``--settle-ms`` of untimed steps (reported) and ``--warmup`` untimed
+steps, then exactly ``--steps`` steps between one event pair, with events at
+up to ten batch boundaries inside for the median and p10/p90 over batches.
+Then each call alone, ``--steps`` times back to back between one event pair
+(``kernels_us``; ``decode_alone_*`` is ``pa_decode``), from which the
+roofline of the partition kernel is taken.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU.
@@ -27,6 +30,7 @@ GPU.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -53,10 +57,8 @@ LONG_PROMPT = 8192
 def _parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=500,
-                   help="untimed steps first (default 500: with 20 the first timed steps still ran about 5%% "
-                        "slower than the steady state on MI355X)")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5, help="untimed steps after the settle phase")
     p.add_argument("--config", default="gqa",
                    choices=["gqa", "mha", "long_fp8", "long_fp8_b32", "tiny", "shared_prefix", "shared_prefix_cow",
                             "shared_prefix_grouped", "shared_prefix_cow_grouped", "shared_prefix_long",
@@ -68,6 +70,17 @@ def _parse():
                         "shared_prefix_cow_grouped (128..512 tried), 1024 for shared_prefix_long_grouped "
                         "(256..1024 tried); 512 for the other workloads, the pages' value for the long-context "
                         "case)")
+    p.add_argument("--settle-ms", type=float, default=1000.0,
+                   help="before --warmup, run untimed steps for at least this many milliseconds (reported in the "
+                        "line). On MI355X the clocks rise from idle over the first second of load; with 5 warm-up "
+                        "steps alone, per-call times drifted by about 5%% between the loops of one run")
+    p.add_argument("--identity-tables", action="store_true",
+                   help="relabel physical blocks so that every sequence's blocks are consecutive (the paging "
+                        "indirection with a trivial layout)")
+    p.add_argument("--paging-ab", action="store_true",
+                   help="instead of the benchmark, time pa_decode with shuffled and with identity block tables, "
+                        "alternating in one process")
+    p.add_argument("--ab-rounds", type=int, default=15)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
     p.add_argument("--pools", type=int, default=2,
@@ -245,16 +258,8 @@ def run_prefill(args):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in evs:
-        e[0].record()
-        calls[0]()
-        e[1].record()
-        calls[1]()
-        e[2].record()
-    torch.cuda.synchronize()
-    scatter_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
-    prefill_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    scatter_us = back_to_back(torch, calls[:1], args.steps)
+    prefill_us = back_to_back(torch, calls[1:], args.steps)
     flops = prefill_flops(wl)
     tflops = flops / (prefill_us * 1e-6) / 1e12
     line = {
@@ -269,6 +274,7 @@ def run_prefill(args):
                    "flops_per_step": flops, "query_tokens": wl.total_q},
         "query_tokens_per_s": round(wl.total_q / (ms * 1e-3), 1),
         "kernels_us": {"reshape_and_cache": round(scatter_us, 2), "prefill": round(prefill_us, 2)},
+        "kernels_timing": "each call alone, back to back between one event pair",
         "roofline": {"kernel": "pa_prefill", "bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "note": "bf16 dense matrix-core peak; the kernel issues 1.5x the algorithmic flops "
@@ -442,16 +448,83 @@ class Device:
         torch.cuda.synchronize()
         return g
 
-    def step(self, i=0, ev=None):
-        if ev is None:
-            for call in self.call_sets[i % len(self.call_sets)]:
-                call()
-            return
-        calls = self.part_sets[i % len(self.part_sets)]  # separate launches, an event around each
-        ev[0].record()
-        for k, call in enumerate(calls):
+    def step(self, i=0):
+        for call in self.call_sets[i % len(self.call_sets)]:
             call()
-            ev[k + 1].record()
+
+
+def settle(run, min_ms):
+    """Untimed steps until at least min_ms of wall time has passed (the GPU
+    raises its clocks over the first hundreds of milliseconds of load);
+    returns (steps, seconds)."""
+    import torch
+    if min_ms <= 0:
+        return 0, 0.0
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        for _ in range(10):
+            run(k)
+            k += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return k, time.perf_counter() - t0
+
+
+def back_to_back(torch, calls, n):
+    """Mean microseconds per call of n calls issued back to back (call i
+    is calls[i % len(calls)]), between one event pair, after a few untimed
+    ones."""
+    for i in range(min(n, 4)):
+        calls[i % len(calls)]()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        calls[i % len(calls)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def identity_tables(wl):
+    """The same workload with every sequence's blocks in consecutive
+    physical blocks: the physical ids are relabelled so that the blocks the
+    tables name, in table order, become 0, 1, 2, ... and the rest follow.
+    Contents, lengths and copy pairs are the same up to the relabelling."""
+    B = wl.block_size
+    named = wl.block_tables[wl.block_tables >= 0]
+    _, first = np.unique(named, return_index=True)
+    used = named[np.sort(first)].astype(np.int64)
+    rest = np.setdiff1d(np.arange(wl.num_blocks, dtype=np.int64), used)
+    new_id = np.empty(wl.num_blocks, np.int64)
+    new_id[np.concatenate([used, rest])] = np.arange(wl.num_blocks, dtype=np.int64)
+    tables = np.where(wl.block_tables >= 0, new_id[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    slots = new_id[wl.slots // B] * B + wl.slots % B
+    pairs = new_id[wl.copy_pairs] if len(wl.copy_pairs) else wl.copy_pairs
+    return dataclasses.replace(wl, block_tables=tables, slots=slots.astype(np.int64),
+                               copy_pairs=pairs.astype(np.int64).reshape(-1, 2))
+
+
+def paging_ab(args):
+    """pa_decode on the same workload with shuffled and with identity block
+    tables, alternating batches of back-to-back calls between the two in one
+    process: the cost of the block-table indirection on this hardware."""
+    import torch
+    wl = _workload(args.config, args.seed, args.partition_size)
+    devs = {"shuffled": Device(wl, pools=args.pools), "identity": Device(identity_tables(wl), pools=args.pools)}
+    settle(devs["shuffled"].step, args.settle_ms)
+    times = {k: [] for k in devs}
+    for _ in range(args.ab_rounds):
+        for name, d in devs.items():
+            times[name].append(back_to_back(torch, d.decode_calls, args.steps))
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    print(json.dumps({
+        "paging_ab": _describe(wl), "rounds": args.ab_rounds, "calls_per_round": args.steps,
+        "pa_decode_us_median": {k: round(v, 2) for k, v in med.items()},
+        "pa_decode_us_p10_p90": {k: [round(float(np.percentile(v, 10)), 2), round(float(np.percentile(v, 90)), 2)]
+                                 for k, v in times.items()},
+        "shuffled_over_identity": round(med["shuffled"] / med["identity"], 4)}), flush=True)
 
 
 def partition_algorithmic_bytes(wl):
@@ -489,32 +562,105 @@ def _traffic(wl):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s):
-    """The float64 oracle on one host core over a bounded sample of the same
-    workload: its sequences in order, starting over after the last one,
-    until the time budget is spent."""
+def _oracle_pools(wl):
+    """The oracle's K/V pools of the workload (its scatter of every token)."""
     import oracle
-    from threadpoolctl import threadpool_limits
-
     kc = np.zeros(wl.pool_shape(), wl.keys.dtype)
     vc = np.zeros(wl.pool_shape(), wl.keys.dtype)
     oracle.reshape_and_cache(kc, vc, wl.keys, wl.values, wl.slots, wl.block_size)
-    done, tokens, elapsed = 0, 0, 0.0
+    return kc, vc
+
+
+def _oracle_rows(wl, kc, vc, first, stride, budget_s):
+    """Run the oracle on rows first, first + stride, ... (wrapping around)
+    until budget_s of its own time is spent; returns (rows, tokens, seconds)."""
+    import oracle
+    done, tokens, elapsed, i = 0, 0, 0.0, first % wl.num_seqs
+    while elapsed < budget_s:
+        t0 = time.perf_counter()
+        oracle.paged_decode(wl.q, wl.q_dtype, kc, vc, wl.kv_dtype, wl.block_tables, wl.seq_lens,
+                            wl.block_size, float(wl.scale), wl.k_scale, wl.v_scale, rows=[i])
+        elapsed += time.perf_counter() - t0
+        done += 1
+        tokens += int(wl.seq_lens[i])
+        i = (i + stride) % wl.num_seqs
+    return done, tokens, elapsed
+
+
+def _oracle_worker(job):
+    """One worker process of the all-cores baseline: the pools come from a
+    shared file, the rest of the workload from the arguments."""
+    wl, pool_file, first, stride, budget_s = job
+    pools = np.load(pool_file, mmap_mode="r")
+    return _oracle_rows(wl, pools[0], pools[1], first, stride, budget_s)
+
+
+def _cpu_share():
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    # one GPU's share of a shared host: at most 16 workers
+    return max(1, min(avail, 16)), avail
+
+
+def cpu_baseline(wl, budget_s):
+    """The float64 oracle, as it stands, over a bounded sample of the same
+    workload: its sequences in order, starting over after the last one, for
+    about budget_s seconds.  Run twice: on one thread, and on all the host
+    cores this GPU's job may use (one spawned worker process per core, each
+    on its own share of the sequences, BLAS limited to one thread per
+    worker, the pools shared through a file in memory).  The worker
+    processes are fresh interpreters that never touch the GPU."""
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing
+    from threadpoolctl import threadpool_limits
+
+    kc, vc = _oracle_pools(wl)
+    kv_per_token = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
     with threadpool_limits(limits=1):
-        while elapsed < budget_s:
-            i = done % wl.num_seqs
-            t0 = time.perf_counter()
-            oracle.paged_decode(wl.q, wl.q_dtype, kc, vc, wl.kv_dtype, wl.block_tables, wl.seq_lens,
-                                wl.block_size, float(wl.scale), wl.k_scale, wl.v_scale, rows=[i])
-            elapsed += time.perf_counter() - t0
-            done += 1
-            tokens += int(wl.seq_lens[i])
-    kv = tokens * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
-    return {"value": round(kv / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequences in order ({done / wl.num_seqs:.2f} passes over the {wl.num_seqs}; "
-                      f"{tokens} tokens, {kv / 1e6:.1f} MB of KV), float64 NumPy, BLAS limited to 1 thread, "
-                      f"{elapsed:.1f} s",
-            "seconds": round(elapsed, 2), "us_per_seq": round(elapsed / done * 1e6, 1)}
+        done, tokens, elapsed = _oracle_rows(wl, kc, vc, 0, 1, budget_s)
+    one = {"value": round(tokens * kv_per_token / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} sequences in order ({done / wl.num_seqs:.2f} passes over the {wl.num_seqs}; "
+                     f"{tokens} tokens, {tokens * kv_per_token / 1e6:.1f} MB of KV), float64 NumPy, "
+                     f"BLAS limited to 1 thread, {elapsed:.1f} s",
+           "seconds": round(elapsed, 2), "us_per_seq": round(elapsed / done * 1e6, 1)}
+    workers, avail = _cpu_share()
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    fd, pool_file = tempfile.mkstemp(suffix=".npy", dir=shm)
+    os.close(fd)
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        np.save(pool_file, np.stack([kc, vc]))
+        del kc, vc
+        os.environ.update({k: "1" for k in saved})  # inherited by the spawned workers
+        # the workers need the queries, tables and lengths, not the token rows
+        slim = dataclasses.replace(wl, keys=wl.keys[:0], values=wl.values[:0], slots=wl.slots[:0],
+                                   step_keys_src=None, step_values_src=None)
+        jobs = [(slim, pool_file, w, workers, budget_s) for w in range(workers)]
+        t0 = time.perf_counter()
+        with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+            parts = list(ex.map(_oracle_worker, jobs))
+        wall = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        os.unlink(pool_file)
+    done_all = sum(p[0] for p in parts)
+    tok_all = sum(p[1] for p in parts)
+    busy = max(p[2] for p in parts)
+    return {"value": round(tok_all * kv_per_token / busy / 1e9, 4), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{done_all} sequences ({done_all / wl.num_seqs:.2f} passes over the {wl.num_seqs}; "
+                      f"{tok_all} tokens, {tok_all * kv_per_token / 1e6:.1f} MB of KV), float64 NumPy, "
+                      f"{workers} worker processes with 1 BLAS thread each, about {busy:.1f} s each",
+            "os_cpu_count": os.cpu_count(), "cores_available": avail, "blas_threads_per_worker": 1,
+            "seconds": round(busy, 2), "wall_s_with_start_up": round(wall, 2),
+            "single_thread": one}
 
 
 def main():
@@ -533,7 +679,12 @@ def main():
     if args.config.startswith("prefill"):
         run_prefill(args)
         return
+    if args.paging_ab:
+        paging_ab(args)
+        return
     wl = _workload(args.config, args.seed, args.partition_size)
+    if args.identity_tables:
+        wl = identity_tables(wl)
     if args.graph and args.pools != 1:
         print("--graph replays one captured step and cannot rotate pool copies; use --pools 1", file=sys.stderr)
         sys.exit(2)
@@ -557,68 +708,54 @@ def main():
         torch.cuda.synchronize()
         graph = dev.capture()
     run = (lambda i: graph.replay()) if graph is not None else dev.step
+    settle_steps, settle_s = settle(run, args.settle_ms)
     for i in range(args.warmup):
-        run(i)
+        run(settle_steps + i)
     torch.cuda.synchronize()
-    # timed region: exactly K steps, no markers between the launches
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: exactly K steps between one event pair; events at batch
+    # boundaries (none inside a batch) give the distribution over batches
+    nb = min(args.steps, 10)
+    bounds = np.linspace(0, args.steps, nb + 1).round().astype(int)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        run(i)
-    stop.record()
+    evs[0].record()
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            run(i)
+        evs[b + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(stop)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = gpu_ms / args.steps
+    batch_us = [evs[b].elapsed_time(evs[b + 1]) / (bounds[b + 1] - bounds[b]) * 1e3 for b in range(nb)]
 
-    # pa_decode alone, back to back (no other launches, no markers between calls)
-    npools = len(dev.decode_calls)
-    for i in range(args.warmup):
-        dev.decode_calls[i % npools]()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record()
-    for i in range(args.steps):
-        dev.decode_calls[i % npools]()
-    d1.record()
-    torch.cuda.synchronize()
-    decode_alone_us = d0.elapsed_time(d1) / args.steps * 1e3
-
-    # per-kernel durations: the same steps, eager, with an event around each launch
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        dev.step(k, evs[k])
-    torch.cuda.synchronize()
-
-    def avg(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs])) * 1e3  # us
-
-    def pct(a, b, q):
-        return float(np.percentile([e[a].elapsed_time(e[b]) for e in evs], q)) * 1e3
-
-    if groups is not None:
-        k_us = {"reshape_and_cache": avg(0, 1), "copy_blocks": avg(1, 2), "decode": avg(2, 3)}
-    else:
-        k_us = {"reshape_and_cache": avg(0, 1), "copy_blocks": avg(1, 2), "decode_partition": avg(2, 3),
-                "decode_reduce": avg(3, 4)}
-        k_us["decode"] = k_us["decode_partition"] + k_us["decode_reduce"]
+    # each call alone, `steps` times back to back between one event pair (no
+    # marker between the launches), alternating the pool copies as the step does
+    n = args.steps
+    decode_alone_us = back_to_back(torch, dev.decode_calls, n)
+    k_us = {"reshape_and_cache": back_to_back(torch, [c[0] for c in dev.part_sets], n),
+            "copy_blocks": back_to_back(torch, [c[1] for c in dev.part_sets], n)}
+    if groups is None:
+        k_us["decode_partition"] = back_to_back(torch, [c[2] for c in dev.part_sets], n)
+        k_us["decode_reduce"] = back_to_back(torch, [c[3] for c in dev.part_sets], n)
+    k_us["decode"] = decode_alone_us
+    if dev.append_fused and groups is None:
+        k_us["decode_append"] = back_to_back(torch, [c[1] for c in dev.call_sets], n)
     kv_bytes = wl.kv_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     if groups is not None:
-        # the three launches together against the distinct bytes they must read
+        # the call's launches together against the distinct bytes they must read
         part_bytes = unique_kv_bytes(wl)
         achieved = part_bytes / (k_us["decode"] * 1e-6) / 1e9
-        roof_kernel = ("pa_decode_shared_prefix (prefix states, partition and reduce launches together) over the "
-                       "distinct K/V bytes")
+        roof_kernel = ("pa_decode_shared_prefix (its launches together, called back to back) over the distinct "
+                       "K/V bytes")
         traffic = None
     else:
         part_bytes = partition_algorithmic_bytes(wl)
         achieved = part_bytes / (k_us["decode_partition"] * 1e-6) / 1e9
-        roof_kernel = ("pa_decode_partition launch (the partition kernel; preceded by decode_plan_kernel "
-                       "above 64 sequences)")
+        roof_kernel = ("decode partition kernel: pa_decode_partition called back to back between one event pair "
+                       "(one launch per call up to 64 sequences; above that a plan kernel precedes it)")
         traffic = _traffic(wl)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -635,9 +772,14 @@ def main():
         "decode_alone_us": round(decode_alone_us, 2),
         "decode_alone_GBs": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9, 2),
         "decode_alone_hbm_frac": round(kv_bytes / (decode_alone_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_us_median": round(float(np.median(batch_us)), 2),
+        "step_us_p10_p90": [round(float(np.percentile(batch_us, 10)), 2),
+                            round(float(np.percentile(batch_us, 90)), 2)],
+        "step_batches": f"{nb} batches of {args.steps // nb}-{-(-args.steps // nb)} steps inside the timed region",
         "kernels_us": {k: round(v, 2) for k, v in k_us.items()},
-        "decode_partition_us_p10_p90" if groups is None else "decode_us_p10_p90":
-            [round(pct(2, 3, 10), 2), round(pct(2, 3, 90), 2)],
+        "kernels_timing": "each call alone, back to back between one event pair",
+        "settle": {"untimed_steps": settle_steps, "seconds": round(settle_s, 3), "min_ms": args.settle_ms,
+                   "why": "untimed steps before --warmup until the GPU clocks have risen from idle"},
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
         "step_calls": (["pa_copy_blocks", "pa_decode_shared_prefix (with the new tokens)" if groups is not None
@@ -646,6 +788,8 @@ def main():
                         "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
                         *([] if groups is not None else ["pa_decode_reduce"])]),
         "pool_copies": args.pools,
+        "block_tables": ("identity: each sequence's blocks are consecutive physical blocks" if args.identity_tables
+                         else "shuffled: blocks drawn from a seeded permutation of the pool"),
         "roofline": {"kernel": roof_kernel, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},

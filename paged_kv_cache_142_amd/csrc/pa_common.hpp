@@ -66,6 +66,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// a * b rounded to float and never fused into a later add.  The online
+// softmax takes its running maximum of the scaled scores and then the
+// exponent of (score - maximum): both must see the same rounded score, or the
+// largest score's weight is 2^(unrounded - rounded) instead of exactly 1
+// (hipcc contracts a * b - c into an fma by default).
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 // Sum over groups of N consecutive lanes (N = 8 or 16, inside one DPP row);
 // every lane of the group receives the group's sum.
 template <int CTRL>

@@ -243,7 +243,7 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
             }
             float sp = c0 + c1;
             sp += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sp), 0x128, 0xf, 0xf, true));  // row_ror:8
-            sp *= qk_scale;
+            sp = mul_rounded(sp, qk_scale);
             if constexpr (MASKED) sp = (row_tok0 + p * TQ + tq < T) ? sp : -INFINITY;
             s[p] = sp;
         }

@@ -496,7 +496,7 @@ decode_partition_kernel(const DecodeArgs a) {
         for (int j = 0; j < Sh::PASSES; ++j) {
             const bool ok = !MASKED || (row_tok0 + j * R + r < T);
 #pragma unroll
-            for (int g = 0; g < G; ++g) s[j][g] = ok ? s[j][g] * qk_scale : -INFINITY;
+            for (int g = 0; g < G; ++g) s[j][g] = ok ? mul_rounded(s[j][g], qk_scale) : -INFINITY;
             if constexpr (MASKED) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[j][e] = ok ? v[j][e] : 0.f;

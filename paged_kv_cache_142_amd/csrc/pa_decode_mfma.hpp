@@ -258,7 +258,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 ok[h][i] = !MASKED || utok0 + 16 * h + 4 * i + g < tok1;
-                s[h][i] = ok[h][i] ? sc[h][i] * qk_scale : -INFINITY;
+                s[h][i] = ok[h][i] ? mul_rounded(sc[h][i], qk_scale) : -INFINITY;
             }
         // ---- online softmax of head n
         float mx = s[0][0];

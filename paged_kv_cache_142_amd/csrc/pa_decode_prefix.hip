@@ -177,8 +177,8 @@ __device__ __forceinline__ void prefix_states(const PrefixArgs& a, unsigned bid)
     }
     const size_t pidx = row * d.max_partitions + part;
     if (g == 0) {
-        store_stream(&d.part_m[pidx], bad ? nan : m);
-        store_stream(&d.part_l[pidx], bad ? nan : l);
+        __builtin_nontemporal_store(bad ? nan : m, &d.part_m[pidx]);
+        __builtin_nontemporal_store(bad ? nan : l, &d.part_l[pidx]);
     }
     const float one = bad ? nan : 1.f;
 #pragma unroll

@@ -105,7 +105,8 @@ const char* pa_status_string(int status);
  *                Two tokens with the same slot in one call: which one lands
  *                is unspecified.
  *   head_dim     64 or 128;  block_size 16 or 32.
- * num_tokens == 0 is a valid no-op.
+ * num_tokens == 0 is a valid no-op.  key, value and the pools must be 16-byte
+ * aligned (PA_ERR_SHAPE otherwise).
  */
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
@@ -131,6 +132,7 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  *   k_scale, v_scale   [num_kv_heads] float32, device
  *   slot_mapping, num_tokens, shapes: as for pa_reshape_and_cache (slots < 0
  *                or past the pool are skipped).
+ * key, value and the pools must be 16-byte aligned (PA_ERR_SHAPE otherwise).
  */
 int pa_reshape_and_cache_fp8(const void* key, const void* value, int src_dtype, void* k_cache,
                              void* v_cache, const float* k_scale, const float* v_scale,

@@ -163,6 +163,8 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_
     if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PA_OK;
     if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    // rows and pool are moved as 16-byte granules
+    if (((uintptr_t)key | (uintptr_t)value | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15u) return PA_ERR_SHAPE;
     const int granules_per_row = head_dim * dtype_bytes(kv_dtype) / 16;
     const int64_t total = (int64_t)num_tokens * 2 * num_kv_heads * granules_per_row;
     const int64_t grid = (total + 255) / 256;
@@ -191,6 +193,8 @@ extern "C" int pa_reshape_and_cache_fp8(const void* key, const void* value, int 
     if (!supported_dim(head_dim) || !supported_block(block_size)) return PA_ERR_UNSUPPORTED;
     if (num_tokens == 0) return PA_OK;
     if (!key || !value || !k_cache || !v_cache || !k_scale || !v_scale || !slot_mapping) return PA_ERR_NULL;
+    // source rows are read, and codes stored, 16 bytes at a time
+    if (((uintptr_t)key | (uintptr_t)value | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15u) return PA_ERR_SHAPE;
     const int groups_per_row = head_dim / 16;
     const int64_t total = (int64_t)num_tokens * 2 * num_kv_heads * groups_per_row;
     const int64_t grid = (total + 255) / 256;

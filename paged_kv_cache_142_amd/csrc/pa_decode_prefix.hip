@@ -74,15 +74,23 @@ __device__ inline GroupShare group_share(const PrefixArgs& a, int grp) {
         const int pre = a.group_prefix[grp];
         const int T0 = d.seq_lens[gs.s0];
         gs.nparts = pre > 0 ? min(pre / P, a.parts) : 0;  // never more than the grid covers
-        if (!length_ok<BS>(d, T0) || T0 < gs.nparts * P) gs.nparts = 0;  // the leader must hold them
+        // the leader must hold them, and with new tokens have a partition of its own (as member_shares)
+        if (!length_ok<BS>(d, T0) || T0 < gs.nparts * P || (d.new_k != nullptr && T0 == gs.nparts * P))
+            gs.nparts = 0;
     }
     return gs;
 }
 
-// whether a member of length T shares the group's partitions
+// whether a member of length T shares the group's partitions.  When the call
+// stores each sequence's newest token, a member must also have a partition of
+// its own (T beyond the shared partitions): the workgroup that computes it is
+// the one that stores the token.  A member whose newest token falls inside the
+// shared partitions breaks the call's contract; it is then computed alone, so
+// that its token is at least stored and its own row is consistent.
 template <int BS>
 __device__ inline bool member_shares(const PrefixArgs& a, const GroupShare& gs, int T) {
-    return gs.nparts > 0 && length_ok<BS>(a.d, T) && T >= gs.nparts * a.d.partition_size;
+    const int shared = gs.nparts * a.d.partition_size;
+    return gs.nparts > 0 && length_ok<BS>(a.d, T) && (a.d.new_k != nullptr ? T > shared : T >= shared);
 }
 
 // The skips of group grp's members, and of the sequences before the first

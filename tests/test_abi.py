@@ -80,6 +80,8 @@ def test_reshape_and_cache_validation(lib):
     assert _rc(lib, block=8) == UNSUP
     for ptr in ("key", "value", "k_cache", "v_cache", "slots"):
         assert _rc(lib, **{ptr: None}) == NULL
+    for ptr in ("key", "value", "k_cache", "v_cache"):  # moved as 16-byte granules
+        assert _rc(lib, **{ptr: FAKE + 8}) == SHAPE
 
 
 def _rq(lib, **kw):
@@ -99,6 +101,8 @@ def test_reshape_and_cache_fp8_validation(lib):
     assert _rq(lib, dim=80) == UNSUP
     for ptr in ("key", "value", "k_cache", "v_cache", "ks", "vs", "slots"):
         assert _rq(lib, **{ptr: None}) == NULL
+    for ptr in ("key", "value", "k_cache", "v_cache"):
+        assert _rq(lib, **{ptr: FAKE + 4}) == SHAPE
 
 
 def _cb(lib, **kw):

@@ -121,23 +121,18 @@ def test_append_invalid_last_block_stores_nothing(heads, kv_heads):
         assert set((blk * 16 + row).tolist()) == slots
 
 
-@pytest.mark.parametrize("heads,kv_heads,fmt,block,P", [
-    (32, 8, "bf16", 16, 256),   # G = 4: the suffix partitions' kernel stores the token
-    (16, 16, "bf16", 16, 256),  # G = 1: copy kernel first
-    (32, 4, "f16", 32, 512),    # G = 8
-    (32, 8, "bf16", 16, 1024),  # 64 blocks per partition: the most the partition kernel stores the token for
-])
-def test_shared_prefix_decode_with_append(heads, kv_heads, fmt, block, P):
-    """pa_decode_shared_prefix given each sequence's newest token: the pools
-    and outputs of the same call over pools that already hold the tokens."""
+def _shared_prefix_append(heads, kv_heads, fmt, block, P, groups, bitwise_out=True):
+    """pa_decode_shared_prefix given each sequence's newest token against the
+    same call over pools that already hold the tokens: bitwise equal pools,
+    and outputs bitwise equal (the same kernels run) or, when the calls share
+    differently, each within tolerance of the oracle."""
     from test_gpu_shared_prefix import _grouped_case
     from gpu_util import poison_device, to_device
 
-    groups = [(2 * P, [2 * P + 5, 2 * P + 90, 2 * P + 1]), (P + 2 * block, [P + 2 * block + 1, P + 100]),
-              (0, [40, 300])]
     lens, tables, starts, prefixes, hk, hv, q = _grouped_case(41, num_heads=heads, num_kv_heads=kv_heads,
                                                               head_dim=128, block_size=block, fmt=fmt, groups=groups)
-    print(f"[case] shared-prefix decode with append H={heads}/{kv_heads} {fmt} B={block} P={P}", flush=True)
+    print(f"[case] shared-prefix decode with append H={heads}/{kv_heads} {fmt} B={block} P={P} "
+          f"groups={[(p, m) for p, m in groups]}", flush=True)
     N, H, d = q.shape
     msl = int(lens.max())
     last_blk = np.array([tables[i, (int(T) - 1) // block] for i, T in enumerate(lens)])
@@ -162,4 +157,36 @@ def test_shared_prefix_decode_with_append(heads, kv_heads, fmt, block, P):
         outs.append(_bytes(out))
         pools.append((_bytes(kc), _bytes(vc)))
     assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
-    assert np.array_equal(outs[0], outs[1])
+    if bitwise_out:
+        assert np.array_equal(outs[0], outs[1])
+        return
+    import oracle
+    expect = oracle.paged_decode(q, fmt, hk, hv, fmt, tables, lens, block, float(np.float32(1.0 / np.sqrt(d))))
+    for o in outs:
+        got = o.view(np.float32).reshape(N, H, d).astype(np.float64)
+        assert_close(got, expect, TOL[fmt], "shared-prefix decode with append vs oracle")
+
+
+@pytest.mark.parametrize("heads,kv_heads,fmt,block,P", [
+    (32, 8, "bf16", 16, 256),   # G = 4: the suffix partitions' kernel stores the token
+    (16, 16, "bf16", 16, 256),  # G = 1: copy kernel first
+    (32, 4, "f16", 32, 512),    # G = 8
+    (32, 8, "bf16", 16, 1024),  # 64 blocks per partition: the most the partition kernel stores the token for
+    (32, 8, "f16", 32, 512),    # G = 4 combined launch, f16, 32-token blocks
+    (32, 8, "bf16", 32, 256),   # G = 4 combined launch, bf16, 32-token blocks
+])
+def test_shared_prefix_decode_with_append(heads, kv_heads, fmt, block, P):
+    groups = [(2 * P, [2 * P + 5, 2 * P + 90, 2 * P + 1]), (P + 2 * block, [P + 2 * block + 1, P + 100]),
+              (0, [40, 300])]
+    _shared_prefix_append(heads, kv_heads, fmt, block, P, groups)
+
+
+@pytest.mark.parametrize("heads,kv_heads", [(32, 8), (16, 16)])
+def test_shared_prefix_append_member_holding_only_shared_partitions(heads, kv_heads):
+    """A group whose only member's newest token falls inside its shared
+    partitions (length exactly the shared partitions; the contract forbids
+    it): the member is computed alone, so its newest token is stored and its
+    row equals the one over a pool that already holds the token."""
+    P, block = 256, 16
+    groups = [(2 * P, [2 * P]), (2 * P, [2 * P + 7, 2 * P + 40]), (P, [3 * P])]
+    _shared_prefix_append(heads, kv_heads, "bf16", block, P, groups, bitwise_out=False)

@@ -248,6 +248,8 @@ def _mixed_groups(rng, P, n_target):
     (32, 4, "f16", 32, 256, 60),    # G = 8
     (16, 16, "bf16", 16, 256, 70),  # G = 1
     (16, 8, "bf16", 32, 512, 50),   # G = 2
+    (32, 8, "f16", 32, 512, 60),    # G = 4 combined launch, f16, 32-token blocks
+    (32, 8, "bf16", 32, 256, 60),   # G = 4 combined launch, bf16, 32-token blocks
 ])
 def test_shared_prefix_decode_groups(heads, kv_heads, fmt, block, P, n):
     seed = heads * 7 + kv_heads + block + P + n

@@ -110,6 +110,15 @@ __device__ __forceinline__ void dma16_to_lds_stream(const void* gptr, uint32_t l
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
+// The same copies from a wavefront-uniform base (held in scalar registers)
+// plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_to_lds_s(const void* sbase, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma16_to_lds_stream_s(const void* sbase, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
 // Store of a partition state, which the reduce kernel reads once right after
 // the partition kernel.  Ordinary stores, so the states may stay in the caches
 // for it: with the non-temporal hint the gqa partition kernel itself ran 2.2%

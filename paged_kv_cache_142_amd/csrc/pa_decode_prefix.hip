@@ -158,7 +158,7 @@ __device__ __forceinline__ void prefix_states(const PrefixArgs& a, unsigned bid)
     t.kvh = kvh;
     t.cvalid[0] = mi < members && member_shares<BS>(a, gs, T);
     t.cpos[0] = t.key_end - 1;
-    t.qptr[0] = (const char*)d.q + (((size_t)seq * d.num_heads + head) * D + 32 * g) * 2;
+    t.qptr[0] = (const char*)d.q + ((size_t)seq * d.num_heads + head) * D * 2;
     t.wave_cols = mem_lo + wave * Sh::PER_WAVE < members;
     t.wpos_min = t.key_end - 1;
     t.wpos_max = t.key_end - 1;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void prefix_states(const PrefixArgs& a, unsigned bid)
     float m1[1], l1[1];
     f32x4 acc1[1][2][4];
     bool bad;
-    mq_tile<KV, D, BS, G, 1, PA_PREFIX_STAGES, true>(a.pool, t, smem, m1, l1, acc1, bad);
+    mq_tile<KV, D, BS, G, 1, PA_PREFIX_STAGES, true, true>(a.pool, t, smem, m1, l1, acc1, bad);
     const float m = m1[0], l = l1[0];
     const f32x4(&acc)[2][4] = acc1[0];
 

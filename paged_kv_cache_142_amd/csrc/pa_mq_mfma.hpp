@@ -17,26 +17,39 @@
 // Per wave, with v_mfma_f32_16x16x32 (bf16 or f16 operands, f32
 // accumulation) and lane = 16 g + n (g = 0..3, n = 0..15):
 //   scores   S^T[key][column] = K Q^T: A = K rows (lane supplies row n of
-//            the 16-key half, elements 32 g + 8 c .. + 7 for the c-th of four
+//            the 16-key half, elements 32 c + 8 g .. + 7 for the c-th of four
 //            products over head_dim 128), B = the wave's query columns.  The
 //            lane receives column n's scores for keys 4 g + i, i = 0..3, of
 //            each half.
-//   softmax  per column: the lane's 8 scores, a max across the four lane
-//            groups, a reference maximum uniform over the column's lanes
-//            that moves (rescaling the accumulators) only when the running
-//            maximum passes it by more than MQ_SLACK; keys after the
-//            column's last visible position get weight 0.
-//   values   O^T[dim][column] += V^T P^T: B = the lane's own p (split into
-//            a 16-bit high part and the rounded remainder, two products, so
-//            p keeps about 16 significant bits); A = V^T, the lane supplying
-//            dim 16 j + n of its 8 keys, delivered in that order by two
-//            transposing LDS reads per 16-dim block j.  The lane receives
-//            column n's dims 16 j + 4 g + i.
+//   softmax  per column: the lane's 8 weights against a reference maximum
+//            uniform over the column's lanes, which moves (rescaling the
+//            accumulators) only when a weight passes 2^MQ_SLACK; keys after
+//            the column's last visible position get weight 0.
+//   values   O^T[dim][column] += V^T P^T: B = the lane's own p; A = V^T,
+//            the lane supplying dim 16 j + n of its 8 keys, delivered in
+//            that order by two transposing LDS reads per 16-dim block j.  The
+//            lane receives column n's dims 16 j + 4 g + i.  Two forms of p
+//            (the SPLIT template argument):
+//            - split: a 16-bit high part and the rounded remainder, two
+//              products, so p keeps about 16 significant bits; the column
+//              sum l adds the unrounded p.
+//            - single: p rounded to the 16-bit format, one product; l is
+//              the sum of the rounded weights, accrued on the matrix cores
+//              (an all-ones A against P^T).  The output is then a convex
+//              combination of the values with each weight off by at most
+//              half an ulp of the format (2^-9 relative for bf16, 2^-12 for
+//              f16), so its error is at most that fraction of the spread of
+//              the values, and no bias remains from a rounded numerator over
+//              an unrounded denominator.
 // K rows sit in LDS XOR-swizzled by 16-byte granule (row t, granule x at
 // slot x ^ (t mod 16)) and V rows by pairs of granules (x ^ 2 (t mod 8)),
 // both through the copies' source addresses, so that the reads above spread
 // over the banks (a transposing read touches one 32-byte dim block of 16
-// rows, whose t mod 8 take every value twice).
+// rows, whose t mod 8 take every value twice).  The K operand's element
+// order matters as much: with granule 4 c + g (the four lane groups of one
+// product read 64 consecutive bytes of their rows) the 16-byte reads run at
+// the full LDS rate on gfx950; with granule 4 g + c they ran at half of it
+// (a read-throughput probe of both patterns).
 //
 // The physical block ids of the key range are loaded into LDS first (in
 // windows of ID_CAP blocks).  An id outside the pool is never used as an
@@ -87,6 +100,18 @@ __device__ __forceinline__ void mq_split8(const float (&p)[8], typename MfmaOps<
         hi[e + 1] = h[1];
         lo[e] = r[0];
         lo[e + 1] = r[1];
+    }
+}
+
+// 8 weights rounded to the 16-bit format, one packed conversion per pair.
+template <Fmt KV>
+__device__ __forceinline__ void mq_round8(const float (&p)[8], typename MfmaOps<KV>::vec& hi) {
+    using pair = typename MfmaOps<KV>::pair;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const pair h = __builtin_convertvector(f32x2{p[e], p[e + 1]}, pair);
+        hi[e] = h[0];
+        hi[e + 1] = h[1];
     }
 }
 
@@ -150,7 +175,9 @@ struct MqShape {
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
     static_assert(CB == 1 || CB == 2, "column blocks per wave");
     static_assert(COPIES % W == 0 && COPIES / 2 % COPIES_PER_WAVE == 0, "a wave copies only K or only V");
+    static_assert(BS % (4 * COPIES_PER_WAVE) == 0, "a wave's copies of one step stay inside one block");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(W * 4 <= 16, "one bad-id flag per wave after the ids");
     static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
     static_assert(S >= 3, "two resident steps (the pipelined loop) plus one being refilled");
     static_assert((S - 2) * COPIES_PER_WAVE <= 63, "vmcnt holds the copies of S - 2 steps");
@@ -160,6 +187,7 @@ struct MqShape {
 // reference its weights are taken against before the reference is moved and
 // the accumulators rescaled: weights stay below 2^8, far from float overflow.
 constexpr float MQ_SLACK = 8.f;
+constexpr float kMqSlackWeight = 256.f;  // 2^MQ_SLACK
 
 // Waits until at most `later` (< N + 1) steps of C copies each, issued after
 // the one needed now, are still in flight.
@@ -207,7 +235,7 @@ struct MqTask {
     int key_end;             // one past the last key any column sees
     int kv_len;              // rows at or beyond this key hold no data
     int kvh;
-    const void* qptr[CB];    // the lane's query elements 32 g .. 32 g + 31 (read only when cvalid)
+    const void* qptr[CB];    // the column's query row (read only when cvalid)
     bool cvalid[CB];         // the lane's column exists
     int cpos[CB];            // last key the lane's column sees
     bool wave_cols;          // the wave has at least one column
@@ -224,7 +252,7 @@ struct MqTask {
 // decode kernels' sense; `bad` is set when the table named a block outside
 // the pool.  All threads of the workgroup must call it.  STREAM marks the
 // K/V copies non-temporal (data read once).
-template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM>
+template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM, bool SPLIT>
 __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, float (&m)[CB], float (&l)[CB],
                         f32x4 (&acc)[CB][2][4], bool& bad) {
     using Sh = MqShape<D, BS, G, CB, STAGES>;
@@ -244,80 +272,105 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     // that the scale c applied below is never negative and max(c s) = c max(s).
     const uint32_t qsign = pool.qk_scale_log2 < 0.f ? 0x80008000u : 0u;
     const float c_scale = fabsf(pool.qk_scale_log2);
-    vec qop[CB][4];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const u32x4* qp = (const u32x4*)t.qptr[cb];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 v = t.cvalid[cb] ? (qp[c] ^ qsign) : u32x4{0, 0, 0, 0};
-            qop[cb][c] = __builtin_bit_cast(vec, v);
-        }
-    }
 
-    // ---- block ids of the key range into LDS, in windows of ID_CAP
+    // ---- block ids of the key range into LDS, in windows of ID_CAP.  Each
+    // wave records in its own flag whether an id it loaded was outside the
+    // pool.  The first window's ids are loaded before the queries: loads
+    // return in order, so the ids can be waited for (and the first copies
+    // issued) while the queries, whose latency is the longest of the tile's
+    // start, are still in flight.
     int* ids = (int*)(smem + Sh::IDS_AT);
-    int* bad_flag = ids + Sh::ID_CAP;
+    int* bad_flags = ids + Sh::ID_CAP;  // [W], written only by their waves
     const int blk0 = t.key_begin / BS;                  // first block of the range
     const int nblk = (t.key_end - 1) / BS + 1 - blk0;   // blocks of the range
-    auto load_ids = [&](int first) {
+    constexpr int IDS_PER_THREAD = Sh::ID_CAP / (Sh::W * 64);
+    bool wave_bad = false;
+    auto fetch_ids = [&](int first, int (&v)[IDS_PER_THREAD]) {
         const int cnt = min(Sh::ID_CAP, nblk - first);
-        for (int j = threadIdx.x; j < cnt; j += 256) {
-            int id = t.bt[blk0 + first + j];
-            if ((unsigned)id >= (unsigned)pool.num_blocks) {
-                *bad_flag = 1;
-                id = 0;
-            }
-            ids[j] = id;
+#pragma unroll
+        for (int r = 0; r < IDS_PER_THREAD; ++r) {
+            const int j = (int)threadIdx.x + r * Sh::W * 64;
+            v[r] = t.bt[blk0 + first + min(j, cnt - 1)];  // (cnt >= 1) entries past cnt are not written
         }
+        return cnt;
     };
-    if (threadIdx.x == 0) *bad_flag = 0;
-    __syncthreads();
+    auto write_ids = [&](const int (&v)[IDS_PER_THREAD], int cnt) {
+        bool out_of_pool = false;
+#pragma unroll
+        for (int r = 0; r < IDS_PER_THREAD; ++r) {
+            const int j = (int)threadIdx.x + r * Sh::W * 64;
+            if (j < cnt) {
+                int id = v[r];
+                if ((unsigned)id >= (unsigned)pool.num_blocks) {
+                    out_of_pool = true;
+                    id = 0;
+                }
+                ids[j] = id;
+            }
+        }
+        wave_bad = wave_bad || __builtin_amdgcn_ballot_w64(out_of_pool) != 0;
+        if (lane == 0) bad_flags[wave] = wave_bad;
+    };
+    auto load_ids = [&](int first) {
+        int v[IDS_PER_THREAD];
+        const int cnt = fetch_ids(first, v);
+        write_ids(v, cnt);
+    };
     int window = 0;  // first block (relative to blk0) held in `ids`
-    load_ids(0);  // in flight together with the query loads above
-    // the queries are resident before the copies start (their waits count copies only)
+    int ids0[IDS_PER_THREAD];
+    const int cnt0 = fetch_ids(0, ids0);
+    __builtin_amdgcn_sched_barrier(0);  // every id load is issued before the query loads
+    // the queries of the lane's columns (converted after the first copies landed)
+    u32x4 qraw[CB][4];
+    vec qop[CB][4];  // [cb][c]: elements 32 c + 8 g .. + 7 of the lane's column
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb) {
+        const u32x4* qp = (const u32x4*)t.qptr[cb] + g;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qop[cb][c]));
-    __syncthreads();
+        for (int c = 0; c < 4; ++c) qraw[cb][c] = qp[4 * c];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    write_ids(ids0, cnt0);
+    // the ids are visible to every wave; the queries may still be in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- copies of one step: wave w copies CPW 1 KiB pieces (waves 0 .. W/2-1
-    // the K pieces, the others the V pieces); each covers 4 rows of 256 bytes.
-    // Everything but the block id is fixed per lane and piece.
+    // the K pieces, the others the V pieces); each covers 4 rows of 256 bytes,
+    // and the CPW pieces of a wave are 4 CPW consecutive rows of one block.
+    // So a wave reads one block id per step (a uniform LDS read) and its
+    // copies differ only in a fixed per-lane offset inside the block.
     const bool wave_v = wave * CPW >= Sh::COPIES / 2;
-    const uint32_t block_bytes = (uint32_t)H * BS * ROWB;
+    const uint64_t block_bytes = (uint64_t)H * BS * ROWB;
     const uint32_t lds0 = lds_addr_of(smem);
-    const char* cp_base[CPW];  // the piece's row and granule in block 0 of the pool
-    int cp_blk[CPW];           // block of the piece's row, relative to the step's first block
+    const int wrow0 = (wave_v ? wave * CPW - Sh::COPIES / 2 : wave * CPW) * 4;  // the wave's first row in the step
+    const int wblk = wrow0 / BS;                                                 // its block, relative to the step's first
+    const char* cp_pool = (const char*)(wave_v ? pool.v_cache : pool.k_cache);
+    uint32_t cp_off[CPW];  // the piece's row and granule inside one block
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-        const int piece = wave * CPW + j;
-        const int pk = wave_v ? piece - Sh::COPIES / 2 : piece;
-        const int row = pk * 4 + lane / 16;   // key row inside the step
-        const int slot = lane % 16;           // 16-byte slot in the LDS row
+        const int row = wrow0 + 4 * j + lane / 16;  // key row inside the step
+        const int slot = lane % 16;                 // 16-byte slot in the LDS row
         const int gran = wave_v ? (slot ^ ((row & 7) << 1)) : (slot ^ (row & 15));
-        cp_blk[j] = row / BS;
-        cp_base[j] = (const char*)(wave_v ? pool.v_cache : pool.k_cache) + ((kvh * BS) + row % BS) * ROWB + gran * 16;
+        cp_off[j] = (uint32_t)(((kvh * BS) + row % BS) * ROWB + gran * 16);
     }
-    // LDS offset of piece j inside a stage (uniform)
-    auto cp_dst = [&](int j) {
-        const int piece = wave * CPW + j;
-        return (uint32_t)((wave_v ? Sh::HALF : 0) + (wave_v ? piece - Sh::COPIES / 2 : piece) * 1024);
+    const uint32_t cp_dst0 = (uint32_t)((wave_v ? Sh::HALF : 0) + wrow0 * ROWB);  // LDS offset inside a stage
+    // the physical block this wave copies for step k (its ids window is loaded)
+    auto read_id = [&](int k) {
+        const int b0 = k * BPS - window;  // the step's first block in `ids`
+        // a block past the range (the step's second, in the last step) rereads the first
+        const int use = k * BPS + wblk < nblk ? b0 + wblk : b0;
+        return ids[use];
     };
-    auto issue = [&](int k, int stage) {
-        const int b0 = k * BPS - window;                              // the step's first block in `ids`
-        const bool whole = k * BPS + BPS <= nblk;                     // uniform: every block of the step exists
+    auto issue = [&](int k, int stage, int id) {
+        const uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane(id);
+        const char* src = cp_pool + pb * block_bytes;
+        const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE) + cp_dst0;
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
-            const int use = (whole || k * BPS + cp_blk[j] < nblk) ? b0 + cp_blk[j] : b0;  // else reread the first
-            const uint32_t pb = (uint32_t)ids[use];
-            const char* src = cp_base[j] + (uint64_t)pb * block_bytes;
-            const uint32_t dst = lds0 + (uint32_t)(stage * Sh::STAGE) + cp_dst(j);
             if constexpr (STREAM)
-                dma16_to_lds_stream(src, dst);
+                dma16_to_lds_stream_s(src, cp_off[j], dst + (uint32_t)(j * 1024));
             else
-                dma16_to_lds(src, dst);
+                dma16_to_lds_s(src, cp_off[j], dst + (uint32_t)(j * 1024));
         }
     };
 
@@ -335,7 +388,7 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     for (int cb = 0; cb < CB; ++cb) cpos[cb] = t.cvalid[cb] ? t.cpos[cb] : -1;  // missing columns see no key
 
     // LDS read offsets that do not depend on the step
-    const int kslot[4] = {(4 * g + 0) ^ n, (4 * g + 1) ^ n, (4 * g + 2) ^ n, (4 * g + 3) ^ n};
+    const int kslot[4] = {(0 + g) ^ n, (4 + g) ^ n, (8 + g) ^ n, (12 + g) ^ n};
 
     auto stage_of = [&](int k) { return smem + (k % S) * Sh::STAGE; };
 
@@ -362,39 +415,76 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     // reference: p = 2^(c s - m) against the column's reference m, which
     // moves to the running maximum only when that exceeds m by more than
     // MQ_SLACK (so p <= 2^MQ_SLACK); l and acc always refer to the current m.
-    // The common path computes p against the current m without waiting for
-    // the maximum; the rare move recomputes them.
+    // The common part computes p against the current m for every column
+    // block without a branch (so that it can run between the value products
+    // of the previous step); the rare move, which also rescales acc, follows
+    // per block and recomputes the weights.
     vec phi[CB], plo[CB];
+    // Without the split, the column sums of the rounded weights accrue on the
+    // matrix cores: lacc[cb] = sum over keys of (all-ones 16 x 32) P^T, every
+    // element the column's sum.
+    f32x4 lacc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) lacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = KV == Fmt::BF16 ? 0x3F803F80u : 0x3C003C00u;  // two 16-bit ones
+    const vec ones = __builtin_bit_cast(vec, u32x4{one2, one2, one2, one2});
     auto softmax = [&](int k, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const int k0 = t.key_begin + k * STEP;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            bool ok[2][4];
+        bool ok[CB][2][4];
+        float l0[CB];
+        bool move[CB];
+        float pmax;  // largest weight of the last weights() call (lane-local)
+        auto weights = [&](int cb, float nmu) {
+            float p[8];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ok[h][i] = !MASKED || k0 + 16 * h + 4 * g + i <= cpos[cb];
-            auto mval = [&](int h, int i) { return ok[h][i] ? sc[cb][h][i] : -INFINITY; };
-            auto weights = [&](float nmu) {
-                float p[8];
+                for (int i = 0; i < 4; ++i) {
+                    p[4 * h + i] = fast_exp2(fmaf(sc[cb][h][i], c_scale, nmu));
+                    if constexpr (MASKED) p[4 * h + i] = ok[cb][h][i] ? p[4 * h + i] : 0.f;
+                }
+            pmax = max3f(max3f(p[0], p[1], p[2]), max3f(p[3], p[4], p[5]), max2f(p[6], p[7]));
+            if constexpr (SPLIT) {
+                mq_split8<KV>(p, phi[cb], plo[cb]);
+                return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            } else {
+                mq_round8<KV>(p, phi[cb]);
+                return 0.f;  // the sum of the rounded weights accrues in lacc
+            }
+        };
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ok[cb][h][i] = !MASKED || k0 + 16 * h + 4 * g + i <= cpos[cb];
+            l0[cb] = l[cb];
+            const bool fresh = m[cb] == -INFINITY;  // no reference yet: weights against 0
+            l[cb] = l0[cb] + weights(cb, fresh ? 0.f : -m[cb]);  // (SPLIT only; else unused)
+            // The reference moves when a weight passes 2^MQ_SLACK, or at the
+            // column's first visible key.  (A weight is 2^(c s - m): it passes
+            // 2^MQ_SLACK exactly when the scaled score passes m + MQ_SLACK, up
+            // to the rounding of the exponent's argument.)
+            bool vis = true;
+            if constexpr (MASKED) {
+                vis = false;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[4 * h + i] = fast_exp2(fmaf(sc[cb][h][i], c_scale, nmu));
-                        if constexpr (MASKED) p[4 * h + i] = ok[h][i] ? p[4 * h + i] : 0.f;
-                    }
-                mq_split8<KV>(p, phi[cb], plo[cb]);
-                return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            };
-            const float l0 = l[cb];
-            l[cb] = l0 + weights(m[cb] == -INFINITY ? 0.f : -m[cb]);
-            float mx = max3f(max3f(mval(0, 0), mval(0, 1), mval(0, 2)), max3f(mval(0, 3), mval(1, 0), mval(1, 1)),
-                             max3f(mval(1, 2), mval(1, 3), -INFINITY));
-            mx = mq_max_groups(mx);
-            const float mxs = mx == -INFINITY ? -INFINITY : mx * c_scale;  // c >= 0: max of the scaled scores
-            if (__builtin_amdgcn_ballot_w64(mxs > m[cb] + MQ_SLACK) != 0) {
+                    for (int i = 0; i < 4; ++i) vis = vis || ok[cb][h][i];
+            }
+            move[cb] = pmax > kMqSlackWeight || (fresh && vis);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            if (__builtin_amdgcn_ballot_w64(move[cb]) != 0) {
+                // the column's largest scaled score (uniform over its lanes)
+                auto mval = [&](int h, int i) { return ok[cb][h][i] ? sc[cb][h][i] : -INFINITY; };
+                float mx = max3f(max3f(mval(0, 0), mval(0, 1), mval(0, 2)), max3f(mval(0, 3), mval(1, 0), mval(1, 1)),
+                                 max3f(mval(1, 2), mval(1, 3), -INFINITY));
+                mx = mq_max_groups(mx);
+                const float mxs = mx == -INFINITY ? -INFINITY : mx * c_scale;  // c >= 0: max of the scaled scores
                 const float mn = fmaxf(m[cb], mxs);
                 const float mu = mn == -INFINITY ? 0.f : mn;
                 const float alpha = fast_exp2(m[cb] - mu);
@@ -402,12 +492,12 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
                 for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) acc[cb][aa][b] *= alpha;
+                if constexpr (!SPLIT) lacc[cb] *= alpha;
                 m[cb] = mn;
-                l[cb] = l0 * alpha + weights(-mu);
+                l[cb] = l0[cb] * alpha + weights(cb, -mu);
             }
         }
     };
-
     // acc += V^T P^T for step k.  The operand of dims 16 j .. 16 j + 15 comes
     // from two transposing LDS reads (ds_read_b64_tr_b16), one per 16-key
     // half h: in each group of 16 lanes, lane l names the 8 bytes of V row
@@ -452,7 +542,13 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 acc[cb][j >> 2][j & 3] = Ops::mma(A, phi[cb], acc[cb][j >> 2][j & 3]);
-                acc[cb][j >> 2][j & 3] = Ops::mma(A, plo[cb], acc[cb][j >> 2][j & 3]);
+                if constexpr (SPLIT) acc[cb][j >> 2][j & 3] = Ops::mma(A, plo[cb], acc[cb][j >> 2][j & 3]);
+            }
+            if constexpr (!SPLIT) {
+                if (j == 0) {
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) lacc[cb] = Ops::mma(ones, phi[cb], lacc[cb]);
+                }
             }
         }
     };
@@ -473,7 +569,11 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
     const int k_vis = __builtin_amdgcn_readfirstlane(t.wave_cols && vis >= 0 ? min(vis / STEP + 1, nsteps) : 0);
 #pragma unroll
     for (int k = 0; k < S - 1; ++k)
-        if (k < nsteps) issue(k, k);
+        if (k < nsteps) issue(k, k, read_id(k));
+    // The id of the next step to copy is read one iteration ahead, so that
+    // its LDS latency is not waited for at the copy; not across a window
+    // boundary (the next window is not loaded yet).
+    int next_id = S - 1 < nsteps ? read_id(S - 1) : 0;
     // wait until this wave's copies of steps <= `need` are complete, then
     // the barrier: everyone's copies up to `need` landed
     auto landed = [&](int need) {
@@ -489,12 +589,25 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
                 window = kn * BPS;
                 load_ids(window);
                 __syncthreads();
+                next_id = read_id(kn);
             }
-            issue(kn, kn % S);
+            issue(kn, kn % S, next_id);
+            if (kn + 1 < nsteps && (kn + 1) % steps_per_window != 0) next_id = read_id(kn + 1);
         }
+    };
+    // Operands of the lane's columns (zero for missing columns).  A negative
+    // score scale is moved into the queries (an exact sign flip), so that the
+    // scale c applied below is never negative and max(c s) = c max(s).
+    auto take_queries = [&] {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                qop[cb][c] = __builtin_bit_cast(vec, t.cvalid[cb] ? (qraw[cb][c] ^ qsign) : u32x4{0, 0, 0, 0});
     };
     if (nsteps > 0) {
         landed(0);
+        take_queries();
         if (k_vis > 0) {
             qk(0);
             if (k_plain > 0)
@@ -524,8 +637,10 @@ __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, flo
         if (k + 1 < k_vis) softmax(k + 1, std::true_type{});
     }
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) l[cb] = mq_sum_groups(l[cb]);
-    bad = *bad_flag != 0;
+    for (int cb = 0; cb < CB; ++cb) l[cb] = SPLIT ? mq_sum_groups(l[cb]) : lacc[cb][0];
+    bad = false;
+#pragma unroll
+    for (int w = 0; w < Sh::W; ++w) bad = bad || bad_flags[w] != 0;
 }
 
 }  // namespace pa

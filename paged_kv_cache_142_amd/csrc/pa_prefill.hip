@@ -21,6 +21,12 @@
 // (high) tile indices empty, and those hold dispatch slots while the long
 // tiles wait.
 //
+// The weights enter the value products as single 16-bit values, normalised
+// by the sum of those rounded weights (the tile's single form): error at most
+// 2^-9 (bf16) or 2^-12 (f16) of the spread of the values a row averages,
+// against 16 significant bits and a second product per value block in the
+// split form (PA_PREFILL_SPLIT=true builds that form instead).
+//
 // A block id outside the pool makes the tile's output rows NaN (the tile
 // never uses it as an address); so does an invalid sequence length.
 #include "pa_mq_mfma.hpp"
@@ -30,6 +36,9 @@
 #endif
 #ifndef PA_PREFILL_STREAM
 #define PA_PREFILL_STREAM false
+#endif
+#ifndef PA_PREFILL_SPLIT
+#define PA_PREFILL_SPLIT false
 #endif
 
 namespace pa {
@@ -167,7 +176,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
         t.cvalid[cb] = ctok[cb] < tok_hi;
         t.cpos[cb] = T - Q + ctok[cb];
         t.qptr[cb] = (const char*)a.q +
-                     (((size_t)(q0 + (t.cvalid[cb] ? ctok[cb] : tok_lo)) * a.num_heads + chead) * D + 32 * g) * 2;
+                     ((size_t)(q0 + (t.cvalid[cb] ? ctok[cb] : tok_lo)) * a.num_heads + chead) * D * 2;
     }
     const int wtok_lo = tok_lo + wave * Sh::PER_WAVE;
     const int wtok_hi = min(wtok_lo + Sh::PER_WAVE, tok_hi);
@@ -178,7 +187,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     float m[PREFILL_CB], l[PREFILL_CB];
     f32x4 acc[PREFILL_CB][2][4];
     bool bad;
-    mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM>(a.pool, t, smem, m, l, acc, bad);
+    mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM, PA_PREFILL_SPLIT>(a.pool, t, smem, m, l, acc, bad);
 
     // ---- output: column n of each block, dims 64 a + 16 b + 4 g + i, four
     // consecutive dims (i = 0..3) per store

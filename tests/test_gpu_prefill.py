@@ -4,7 +4,11 @@ matrix cores) against the float64 oracle.
 Every test fills the pool (0xFF poison first) through pa_reshape_and_cache:
 each sequence's context, then the step's chunk, and compares every output
 row with the oracle's causal attention over the same pool, within 1e-2
-(bf16/fp16 KV)."""
+(bf16/fp16 KV).  The kernel multiplies the values by the weights rounded to
+the K/V format and divides by the sum of those rounded weights, so a row is
+a convex combination of its values whose weights are each off by at most half
+an ulp of the format (2^-9 relative for bf16): its error is at most 2^-9 times
+the spread of the values it averages, about 4e-3 on these N(0, 1) inputs."""
 
 import numpy as np
 import pytest
@@ -108,13 +112,31 @@ def test_prefill_zero_query_sequences_and_out_formats():
         case = PrefillCase(wl, out_fmt=fmt)
         case.run()
         got = out_as_f64(case.out)
-        rounded = torch.from_numpy(want).to(dt).double().numpy()
-        assert np.max(np.abs(got - rounded)) <= TOL["bf16"]
+        # the 1e-2 bar holds before the output is rounded to its format, and
+        # rounding to nearest moves a value by at most half an ulp there
+        half_ulp = np.ldexp(0.5, np.frexp(np.maximum(np.abs(got), np.abs(want)))[1] - (8 if fmt == "bf16" else 11))
+        err = np.abs(got - want)
+        print(f"[parity] prefill out {fmt}: max abs err {err.max():.3e}, max of err - half ulp "
+              f"{(err - half_ulp).max():.3e} (tol 1e-02)", flush=True)
+        assert np.all(err <= TOL["bf16"] + half_ulp)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_prefill_extreme_logits(kv):
+    """Query rows rescaled so that each row's largest visible logit reaches
+    +-80: the weights span many binades and a few keys dominate, the case
+    where rounding the weights to the K/V format matters most."""
+    wl = workloads.build_prefill_workload(f"prefill_extreme_{kv}", 11, seq_lens=[1, 2, 37, 300, 513],
+                                          query_lens=[1, 2, 37, 150, 64], num_heads=32, num_kv_heads=8,
+                                          head_dim=128, block_size=16, kv_dtype=kv, q_dtype=kv, logit_target=80.0)
+    _check(wl)
 
 
 def test_last_row_matches_pa_decode():
     """The last query row of a chunk attends to every cached token: it must
-    agree with pa_decode's output for that sequence."""
+    agree with pa_decode's output for that sequence, to the sum of the two
+    kernels' error bounds against the oracle (pa_decode keeps about 16
+    significant bits of each weight, pa_prefill the K/V format's 8)."""
     wl = workloads.prefill(4, num_seqs=5, max_len=900, chunk=64)
     c = wl.cache
     case = PrefillCase(wl)
@@ -127,7 +149,7 @@ def test_last_row_matches_pa_decode():
     pa.pa_decode(out, q_last, case.k_cache, case.v_cache, case.tables, case.lens, c.max_seq_len, float(c.scale), 512,
                  ws)
     torch.cuda.synchronize()
-    assert np.max(np.abs(out_as_f64(out) - out_as_f64(case.out[last]))) < 2e-5
+    assert_close(out_as_f64(case.out[last]), out_as_f64(out), TOL["bf16"], "last prefill row vs pa_decode")
 
 
 def test_prefill_long_context_crosses_id_windows():

@@ -111,3 +111,22 @@ def test_edge_lengths_with_empty_sequence():
                                partition_size=32)
     _structure(wl)
     assert np.all(wl.block_tables[0] == -1)
+
+
+def test_prefill_logit_target_reaches_the_target():
+    """Each query row's largest visible |scale q.k| is the target, up to the
+    rounding of q to bf16 (relative 2^-8 per element)."""
+    wl = workloads.build_prefill_workload("px", 3, seq_lens=[5, 40], query_lens=[5, 17], num_heads=4,
+                                          num_kv_heads=2, head_dim=16, block_size=16, kv_dtype="bf16",
+                                          q_dtype="bf16", logit_target=80.0)
+    c = wl.cache
+    q = torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    k = torch.from_numpy(c.keys.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for i in range(c.num_seqs):
+        T, Q = int(c.seq_lens[i]), int(wl.query_lens[i])
+        keys = k[c.token_offsets[i]:c.token_offsets[i + 1]]
+        for j in range(Q):
+            pos = T - Q + j
+            for h in range(4):
+                top = np.abs(keys[:pos + 1, h // 2, :] @ q[wl.query_start[i] + j, h]).max() * float(c.scale)
+                assert abs(top - 80.0) <= 80.0 * 2.0 ** -6, (i, j, h, top)

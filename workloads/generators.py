@@ -391,9 +391,14 @@ class PrefillWorkload:
 
 
 def build_prefill_workload(name, seed, *, seq_lens, query_lens, num_heads, num_kv_heads, head_dim, block_size,
-                           kv_dtype, q_dtype, spare_blocks=0):
+                           kv_dtype, q_dtype, spare_blocks=0, logit_target=None):
     """Assemble a ``PrefillWorkload``: the cache as for decode (seeded), plus
-    N(0, 1) query rows for each sequence's last ``query_lens[i]`` tokens."""
+    N(0, 1) query rows for each sequence's last ``query_lens[i]`` tokens.
+
+    With ``logit_target``, each query row (token, head) is rescaled, before
+    rounding to ``q_dtype``, so that its largest ``|scale * q . k|`` over the
+    keys it sees (the sequence's keys up to its own position) equals the
+    target: an extreme-logit stress input."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     query_lens = np.asarray(query_lens, dtype=np.int32)
     if np.any(query_lens < 0) or np.any(query_lens > seq_lens):
@@ -404,7 +409,22 @@ def build_prefill_workload(name, seed, *, seq_lens, query_lens, num_heads, num_k
     start = np.zeros(len(query_lens) + 1, dtype=np.int32)
     start[1:] = np.cumsum(query_lens)
     rng = np.random.default_rng(_seed(seed, 20))
-    q = round_to_storage(rng.standard_normal((int(start[-1]), num_heads, head_dim), dtype=np.float32), q_dtype)
+    q32 = rng.standard_normal((int(start[-1]), num_heads, head_dim), dtype=np.float32)
+    if logit_target is not None:
+        group = num_heads // num_kv_heads
+        for i, (T, Q) in enumerate(zip(seq_lens.astype(np.int64), query_lens.astype(np.int64))):
+            if Q == 0:
+                continue
+            raw = cache.keys[cache.token_offsets[i]:cache.token_offsets[i + 1]]
+            kf = torch.from_numpy(raw.view(np.int16)).view(
+                torch.bfloat16 if kv_dtype == "bf16" else torch.float16).to(torch.float64).numpy()
+            rows = q32[start[i]:start[i + 1]].astype(np.float64)       # [Q][H][d]
+            for h in range(num_heads):
+                logit = np.abs(rows[:, h, :] @ kf[:, h // group, :].T) * float(cache.scale)  # [Q][T]
+                visible = np.arange(T)[None, :] <= (T - Q + np.arange(Q))[:, None]
+                mag = np.where(visible, logit, 0.0).max(axis=1)
+                q32[start[i]:start[i + 1], h, :] = (rows[:, h, :] * (logit_target / mag)[:, None]).astype(np.float32)
+    q = round_to_storage(q32, q_dtype)
     return PrefillWorkload(cache=cache, query_lens=query_lens, query_start=start, q=q)
 
 

@@ -277,8 +277,9 @@ def run_prefill(args):
         "kernels_timing": "each call alone, back to back between one event pair",
         "roofline": {"kernel": "pa_prefill", "bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
-                     "note": "bf16 dense matrix-core peak; the kernel issues 1.5x the algorithmic flops "
-                             "(hi/lo halves of p) and computes masked keys of the diagonal steps"},
+                     "note": "bf16 dense matrix-core peak; the kernel issues 34 matrix products per 32 "
+                             "algorithmic ones (2 accrue the column sums of the rounded weights) and computes "
+                             "the masked keys of the diagonal steps"},
     }
     print(json.dumps(line), flush=True)
 

@@ -66,7 +66,7 @@ def _parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--partition-size", type=int, default=None,
                    help="split-KV partition size (default: the fastest in same-box sweeps where the workload "
-                        "leaves it open: 768 for gqa (512..1024 tried), 256 for shared_prefix_grouped and "
+                        "leaves it open: 832 for gqa (512..1024 tried), 256 for shared_prefix_grouped and "
                         "shared_prefix_cow_grouped (128..512 tried), 1024 for shared_prefix_long_grouped "
                         "(256..1024 tried); 512 for the other workloads, the pages' value for the long-context "
                         "case)")
@@ -287,7 +287,7 @@ def run_prefill(args):
 def _workload(name, seed, partition_size):
     import workloads
     if partition_size is None:
-        partition_size = {"gqa": 768, "shared_prefix_grouped": 256, "shared_prefix_cow_grouped": 256,
+        partition_size = {"gqa": 832, "shared_prefix_grouped": 256, "shared_prefix_cow_grouped": 256,
                           "shared_prefix_long_grouped": 1024}.get(name, 512)
     if name.startswith("shared_prefix_cow"):
         return shared_prefix_step(seed, partition_size, 1032)

@@ -186,7 +186,7 @@ def _sample_rows(wl, k, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("seed,partition_size", [(0, 768), (0, 512), (1, 768), (2, 768)])
+@pytest.mark.parametrize("seed,partition_size", [(0, 832), (0, 768), (0, 512), (1, 832), (2, 832)])
 def test_gqa_full_size_all_rows(seed, partition_size):
     _run_and_check(workloads.gqa(seed, partition_size=partition_size))
 

@@ -242,9 +242,9 @@ def tiny(seed=0):
                                  spare_blocks=0, num_copy_pairs=3, partition_size=512, pool_size=32)
 
 
-def gqa(seed=0, num_seqs=64, max_len=4096, partition_size=768):
+def gqa(seed=0, num_seqs=64, max_len=4096, partition_size=832):
     """bf16, 32 query / 8 kv heads, d=128, B=16, lengths uniform on 1..4096,
-    split-KV partitions of 768 tokens (the benchmarked configuration)."""
+    split-KV partitions of 832 tokens (the benchmarked configuration)."""
     lens = np.random.default_rng(_seed(seed, 0)).integers(1, max_len + 1, size=num_seqs)
     return build_decode_workload("gqa", seed, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
                                  block_size=16, kv_dtype="bf16", q_dtype="bf16", spare_blocks=16,

@@ -119,12 +119,16 @@ __device__ __forceinline__ void dma16_to_lds_stream_s(const void* sbase, uint32_
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
-// Store of a partition state, which the reduce kernel reads once right after
-// the partition kernel.  Ordinary stores, so the states may stay in the caches
-// for it: with the non-temporal hint the gqa partition kernel itself ran 2.2%
-// slower (92.3 against 90.3 us, same-box interleaved A/B) and the FP8
-// long-context decode 0.8% slower.
+// Stores of a partition state, which the reduce kernel reads once right after
+// the partition kernel.  Which hint pays depends on the kernel (same-box
+// interleaved A/Bs, three rounds each): the GQA-4 kernel, whose states are
+// few (3.3 MB on the gqa workload), runs 3% faster with ordinary stores that
+// may leave them in the caches for the reduce (89.2 against 91.9 us); the
+// generic kernel on the mha workload, which writes 21 MB of states, runs 3.2%
+// faster with the non-temporal hint (881 against 910 us), and the FP8
+// matrix-core kernel 0.7% faster (195.0 against 196.6 us).
 __device__ __forceinline__ void store_state(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_state_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>

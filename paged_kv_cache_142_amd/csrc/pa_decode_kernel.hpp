@@ -575,10 +575,10 @@ decode_partition_kernel(const DecodeArgs a) {
         } else {
             const size_t pidx = row * a.max_partitions + part;
             if (d == 0) {
-                store_state(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
-                store_state(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
+                store_state_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
+                store_state_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
             }
-            store_state(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
+            store_state_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     };
 

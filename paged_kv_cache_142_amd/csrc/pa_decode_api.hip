@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const Dec
     const int c4 = rt - pg * C4;
     const size_t row = (size_t)blockIdx.x * RPW + rw;
     const bool in_grid = row < (size_t)a.num_seqs * a.num_heads;
-    const int seq = in_grid ? (int)(row / a.num_heads) : 0;
+    const int seq = in_grid ? (int)((unsigned)row / (unsigned)a.num_heads) : 0;  // in the grid: row < 2^31
     const int T = in_grid ? a.seq_lens[seq] : 0;
     auto store4 = [&](float4 o) {
         const size_t idx = row * D + 4 * c4;

@@ -350,9 +350,11 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     if (lane == 0) winv[wave] = invalid;
     if (half == 0 && tq == 0) { wm[wave * G + hl] = m; wl[wave * G + hl] = l; }
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wacc[((wave * R + r) * G + g) * D + Row::dim(c, e)] = acc[g][e];
+    for (int g = 0; g < G; ++g) {
+        float* row = wacc + ((wave * R + r) * G + g) * D;
+        *(float4*)(row + merge_pos(Row::dim(c, 0))) = float4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
+        *(float4*)(row + merge_pos(Row::dim(c, 4))) = float4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
+    }
     __syncthreads();
     int bad = 0;
 #pragma unroll
@@ -371,7 +373,7 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
             const float f = fast_exp2(wm[w * G + g] - mu);
             float rows = 0.f;
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) rows += wacc[((w * R + rr) * G + g) * D + d];
+            for (int rr = 0; rr < R; ++rr) rows += wacc[((w * R + rr) * G + g) * D + merge_pos(d)];
             L = fmaf(f, wl[w * G + g], L);
             A = fmaf(f, rows, A);
         }

@@ -181,6 +181,15 @@ __device__ __forceinline__ void store_out(void* out, int dtype, size_t idx, floa
         ((_Float16*)out)[idx] = (_Float16)v;
 }
 
+// Position of element d of a row of the waves' merge area in LDS: in every
+// odd stretch of 32 elements the 16-byte granules swap in pairs.  A lane
+// holds 8 consecutive elements of a row (granules 2c and 2c + 1) and writes
+// them with two 16-byte stores.  A 16-byte store goes to LDS eight lanes at a
+// time over 128 bytes of banks, so unswapped the lanes c and c + 4 of each
+// eight would hit the same banks.  Rows read by consecutive threads still
+// cover each bank once.
+__device__ __forceinline__ int merge_pos(int d) { return d ^ (((d >> 5) & 1) << 2); }
+
 // Placement of a lane's 8 elements inside one token row of format KV.
 template <Fmt KV, int D>
 struct LaneRow {
@@ -602,9 +611,11 @@ decode_partition_kernel(const DecodeArgs a) {
         }
         if (r == 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) wacc[(wave * G + g) * D + Row::dim(c, e)] = acc[g][e];
+            for (int g = 0; g < G; ++g) {
+                float* row = wacc + (wave * G + g) * D;  // elements e < 4 and e >= 4 are 4 consecutive dims each
+                *(float4*)(row + merge_pos(Row::dim(c, 0))) = float4{acc[g][0], acc[g][1], acc[g][2], acc[g][3]};
+                *(float4*)(row + merge_pos(Row::dim(c, 4))) = float4{acc[g][4], acc[g][5], acc[g][6], acc[g][7]};
+            }
         }
         __syncthreads();
         int bad = 0;
@@ -622,7 +633,7 @@ decode_partition_kernel(const DecodeArgs a) {
             for (int w = 0; w < W; ++w) {
                 const float f = fast_exp2(wm[w * G + g] - mu);
                 L = fmaf(f, wl[w * G + g], L);
-                A = fmaf(f, wacc[(w * G + g) * D + d], A);
+                A = fmaf(f, wacc[(w * G + g) * D + merge_pos(d)], A);
             }
             emit(g, d, M, L, A, bad);
         }

@@ -354,12 +354,14 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     if (lane == 0) winv[wave] = invalid;
     if (n < G) {
         if (g == 0) { wm[wave * G + n] = m; wl[wave * G + n] = l; }
-        float* dst = wacc + (wave * G + n) * D + 16 * g;
+        // granule x (columns 4x .. 4x + 3) of head n's row sits at x ^ n, so
+        // that the eight heads' stores of one instruction spread over the banks
+        float* dst = wacc + (wave * G + n) * D;
 #pragma unroll
         for (int aa = 0; aa < NA; ++aa)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                *(float4*)(dst + 64 * aa + 4 * i) =
+                *(float4*)(dst + ((16 * aa + 4 * g + i) ^ n) * 4) =
                     float4{acc[aa][0][i], acc[aa][1][i], acc[aa][2][i], acc[aa][3][i]};
     }
     __syncthreads();
@@ -380,7 +382,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
         for (int w = 0; w < W; ++w) {
             const float f = fast_exp2(wm[w * G + hg] - mu);
             L = fmaf(f, wl[w * G + hg], L);
-            A = fmaf(f, wacc[(w * G + hg) * D + d], A);
+            A = fmaf(f, wacc[(w * G + hg) * D + (d ^ (hg << 2))], A);
         }
         const size_t row = (size_t)seq * a.num_heads + hq0 + hg;
         if (n_parts == 1) {

@@ -3,10 +3,12 @@
 A step is one pass of the whole path over the batch: the step's block
 copies (``pa_copy_blocks``), the scatter of each sequence's new token into
 the pool, and the decode itself.  Where one call can do the last two
-(bf16/f16/f32 pools), the step is ``pa_copy_blocks`` then
-``pa_decode_append`` (or ``pa_decode_shared_prefix`` given the new tokens,
-for the grouped shared-prefix workloads), which stores the tokens inside the
-partition kernel for four query heads per kv head; for FP8 pools (quantized
+(bf16/f16/f32 pools), the step is one ``pa_decode_append_cow`` call: for
+four query heads per kv head its partition launch also makes the copies
+and stores the tokens, elsewhere it is ``pa_copy_blocks`` then
+``pa_decode_append`` (``--separate-cow``: those two calls everywhere).  The
+grouped shared-prefix workloads run ``pa_copy_blocks`` then
+``pa_decode_shared_prefix`` given the new tokens.  For FP8 pools (quantized
 on write) it is the scatter (``pa_reshape_and_cache_fp8``), the copies, and
 the decode (``pa_decode_partition`` then ``pa_decode_reduce``).
 ``step_calls`` in the output names them.
@@ -86,6 +88,9 @@ def _parse():
     p.add_argument("--pools", type=int, default=2,
                    help="copies of the K/V pool; step i uses copy i %% pools, so back-to-back steps read K/V that "
                         "the 256 MB Infinity Cache does not hold (1: every step re-reads the same pool)")
+    p.add_argument("--separate-cow", action="store_true",
+                   help="issue the step's copy-on-write copies as a pa_copy_blocks launch before pa_decode_append "
+                        "instead of inside pa_decode_append_cow")
     p.add_argument("--graph", action="store_true",
                    help="replay the step as a captured HIP graph (the four launches) instead of eager calls")
     p.add_argument("--swap-mib", type=int, default=0,
@@ -328,7 +333,7 @@ class Device:
     K/V in the 256 MB Infinity Cache (MALL) once the copies together exceed it.
     """
 
-    def __init__(self, wl, pools=1, groups=None):
+    def __init__(self, wl, pools=1, groups=None, separate_cow=False):
         import torch
         import paged_kv_cache_142_amd as pa
         self.pa, self.torch, self.wl = pa, torch, wl
@@ -393,10 +398,17 @@ class Device:
         # that call applies; the per-call timing loop keeps the four separate
         # launches (scatter, copy, partition, reduce).
         self.append_fused = not self.quantize_step and self.step_keys.shape[0] == wl.num_seqs
+        # the copy-on-write copies inside that call (pa_decode_append_cow), or
+        # as a launch of their own before it
+        self.separate_cow = separate_cow
         # identical calls every step: marshal the C arguments once per pool copy
         self.call_sets = [self._make_calls(kc, vc, fused=self.append_fused) for kc, vc in self.pools]
         self.part_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
         self.decode_calls = [self._decode_call(kc, vc) for kc, vc in self.pools]
+        # decode with append alone (no copies), for the per-call times
+        self.append_calls = ([self.pa.prepared("pa_decode_append", **dict(self.dargs, k_cache=kc, v_cache=vc),
+                                               key=self.step_keys, value=self.step_values) for kc, vc in self.pools]
+                             if self.append_fused and self.groups is None else [])
         self.calls = self.call_sets[0]
         torch.cuda.synchronize()
 
@@ -417,7 +429,10 @@ class Device:
             if self.groups is not None:
                 return [copy, pa.prepared("pa_decode_shared_prefix", **dargs, **self.groups, key=self.step_keys,
                                           value=self.step_values)]
-            return [copy, pa.prepared("pa_decode_append", **dargs, key=self.step_keys, value=self.step_values)]
+            if self.separate_cow:
+                return [copy, pa.prepared("pa_decode_append", **dargs, key=self.step_keys, value=self.step_values)]
+            return [pa.prepared("pa_decode_append_cow", **dargs, key=self.step_keys, value=self.step_values,
+                                block_pairs=self.pairs)]
         scatter = (pa.prepared("pa_reshape_and_cache_fp8", self.step_keys, self.step_values, kc, vc,
                                self.k_scale, self.v_scale, self.step_slots)
                    if self.quantize_step else
@@ -702,7 +717,7 @@ def main():
         shared = np.array([min(prompt_len // B * B, int((wl.seq_lens[a:b] - 1).min()) // B * B)
                            for a, b in zip(starts[:-1], starts[1:])], np.int32)
         groups = (starts, shared)
-    dev = Device(wl, pools=args.pools, groups=groups)
+    dev = Device(wl, pools=args.pools, groups=groups, separate_cow=args.separate_cow)
     graph = None
     if args.graph:  # one eager step first (one-time kernel attribute setup), then capture
         dev.step()
@@ -741,8 +756,10 @@ def main():
         k_us["decode_partition"] = back_to_back(torch, [c[2] for c in dev.part_sets], n)
         k_us["decode_reduce"] = back_to_back(torch, [c[3] for c in dev.part_sets], n)
     k_us["decode"] = decode_alone_us
-    if dev.append_fused and groups is None:
-        k_us["decode_append"] = back_to_back(torch, [c[1] for c in dev.call_sets], n)
+    if dev.append_calls:
+        k_us["decode_append"] = back_to_back(torch, dev.append_calls, n)
+        if not dev.separate_cow:
+            k_us["decode_append_cow"] = back_to_back(torch, [c[0] for c in dev.call_sets], n)
     kv_bytes = wl.kv_bytes()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     if groups is not None:
@@ -783,8 +800,10 @@ def main():
                    "why": "untimed steps before --warmup until the GPU clocks have risen from idle"},
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "step_mode": "hip_graph" if graph is not None else "eager",
-        "step_calls": (["pa_copy_blocks", "pa_decode_shared_prefix (with the new tokens)" if groups is not None
-                        else "pa_decode_append"] if dev.append_fused else
+        "step_calls": ((["pa_copy_blocks", "pa_decode_shared_prefix (with the new tokens)"] if groups is not None
+                        else ["pa_copy_blocks", "pa_decode_append"] if dev.separate_cow
+                        else ["pa_decode_append_cow (the copies in the decode launch for four query heads per kv "
+                              "head; otherwise pa_copy_blocks, then pa_decode_append)"]) if dev.append_fused else
                        ["pa_reshape_and_cache" + ("_fp8" if dev.quantize_step else ""), "pa_copy_blocks",
                         "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
                         *([] if groups is not None else ["pa_decode_reduce"])]),

@@ -346,6 +346,42 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
                      void* stream, const void* key, const void* value);
 
 /*
+ * pa_decode_append_cow -- pa_copy_blocks, then pa_decode_append, in one
+ * launch where possible.
+ *
+ * A decode step of a batch with copy-on-write (the explainer's section
+ * "Copy-on-Write（CoW）によるメモリ共有": a sequence about to write into a
+ * shared block gets a private copy first) copies those blocks, stores each
+ * sequence's new token and attends.  The result and the pool are bitwise
+ * those of pa_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, ...)
+ * followed by pa_decode_append with the same arguments.
+ *
+ * Where pa_decode_append stores the tokens inside the GQA-4 partition kernel
+ * (bf16 or f16 K/V, four query heads per kv head, head_dim 64 or 128, block
+ * size 16 or 32, at most 64 blocks per partition) and num_pairs <= 16, the
+ * copies run in the same launch: its last 2 num_pairs workgroups copy the
+ * pairs (K and V), the partition workgroups read a destination block from
+ * its source (the same content once copied), and when a destination is a
+ * sequence's last block its copying workgroup stores that sequence's new
+ * token into it after the copy.  Other shapes make the two calls.
+ *   block_pairs  int64 [num_pairs][2] (source, destination), device; pairs
+ *                outside the pool are skipped, as by pa_copy_blocks
+ *   num_pairs    >= 0; 0 makes this pa_decode_append
+ *   other arguments: as for pa_decode_append.  Preconditions of
+ *                pa_copy_blocks: destinations are distinct and none is a
+ *                source; a destination belongs to at most one sequence.
+ * Errors: PA_ERR_SHAPE for num_pairs < 0, PA_ERR_NULL for a null block_pairs
+ * with num_pairs > 0, otherwise those of the two calls.
+ */
+int pa_decode_append_cow(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
+                         const void* v_cache, int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int max_seq_len, int num_seqs, int num_heads,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                         const float* k_scale, const float* v_scale, int partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream, const void* key, const void* value,
+                         const int64_t* block_pairs, int num_pairs);
+
+/*
  * pa_decode_shared_prefix -- pa_decode for batches whose sequences share
  * prompt blocks (parallel samples and beams forked from one prompt), reading
  * each shared block once per group instead of once per sequence.

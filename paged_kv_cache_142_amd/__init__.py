@@ -156,6 +156,9 @@ def prepared(name, *args, **kw):
     elif name == "pa_decode_append":
         key, value = kw.pop("key"), kw.pop("value")
         argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
+    elif name == "pa_decode_append_cow":
+        key, value, pairs = kw.pop("key"), kw.pop("value"), kw.pop("block_pairs")
+        argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw) + _pairs_argv(pairs)
     elif name == "pa_decode_shared_prefix":
         gs, gp, mgs, mpl = (kw.pop(k) for k in ("group_start", "group_prefix", "max_group_size", "max_prefix_len"))
         key, value = kw.pop("key", None), kw.pop("value", None)
@@ -231,6 +234,22 @@ def pa_decode_append(*args, key, value, **kw):
     ``seq_lens - 1``; the other arguments are ``pa_decode``'s."""
     argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
     _check(_lib.load().pa_decode_append(*argv), "pa_decode_append")
+
+
+def pa_decode_append_cow(*args, key, value, block_pairs, **kw):
+    """``pa_copy_blocks`` with ``block_pairs`` (int64 ``[P][2]`` (source,
+    destination), device), then ``pa_decode_append``; one launch where the
+    GQA-4 kernel stores the new tokens."""
+    argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw) + _pairs_argv(block_pairs)
+    _check(_lib.load().pa_decode_append_cow(*argv), "pa_decode_append_cow")
+
+
+def _pairs_argv(block_pairs):
+    if block_pairs is None:
+        return (None, 0)
+    if block_pairs.dtype != torch.int64 or block_pairs.numel() % 2:
+        raise ValueError("block_pairs must be int64 (source, destination) pairs")
+    return (_ptr(block_pairs), int(block_pairs.numel() // 2))
 
 
 def pa_decode_shared_prefix(*args, group_start, group_prefix, max_group_size, max_prefix_len, key=None, value=None,

@@ -37,6 +37,7 @@ SIGNATURES = {
     "pa_decode_partition": (_c_int, _DECODE_ARGS),
     "pa_decode_reduce": (_c_int, _DECODE_ARGS),
     "pa_decode_append": (_c_int, _DECODE_ARGS + [_vp, _vp]),
+    "pa_decode_append_cow": (_c_int, _DECODE_ARGS + [_vp, _vp, _vp, _c_int]),
     "pa_decode_shared_prefix": (_c_int, _DECODE_ARGS + [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
 }
 

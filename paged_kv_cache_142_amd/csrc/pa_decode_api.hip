@@ -312,6 +312,8 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
     a.skip_parts = nullptr;
     a.new_k = nullptr;
+    a.cow_pairs = nullptr;
+    a.cow_num = 0;
     a.new_v = nullptr;
     pr.head_dim = head_dim;
     pr.group = group;
@@ -477,6 +479,42 @@ extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* v
     const hipStream_t s = (hipStream_t)stream;
     const int s0 = pa::prepare_append(pr, key, value, (void*)k_cache, (void*)v_cache, head_dim, s);
     if (s0 != PA_OK) return s0;
+    const int s1 = pa::run_partition(pr, s);
+    if (s1 != PA_OK) return s1;
+    return pa::run_reduce(pr, s);
+}
+
+// Copy-on-write copies and decode with append in one launch where the
+// GQA-4 kernel stores the new tokens; elsewhere pa_copy_blocks, then
+// pa_decode_append.
+extern "C" int pa_decode_append_cow(PA_DECODE_PARAMS, const void* key, const void* value,
+                                    const int64_t* block_pairs, int num_pairs) {
+    if (num_pairs < 0) return PA_ERR_SHAPE;
+    if (num_pairs > 0 && !block_pairs) return PA_ERR_NULL;
+    pa::Prepared pr;
+    const int st = pa::prepare(pr, PA_DECODE_ARGS);
+    if (st != PA_OK) return st;
+    const bool fused = num_pairs > 0 && !pr.nothing_to_do && pr.args.max_partitions > 0 &&
+                       num_pairs <= pa::COW_MAX_PAIRS && pa::partition_appends(pr) &&
+                       (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+    if (!fused) {
+        const int c = pa_copy_blocks((void*)k_cache, (void*)v_cache, block_pairs, num_pairs, num_kv_heads,
+                                     head_dim, block_size, num_blocks, kv_dtype, stream);
+        if (c != PA_OK) return c;
+        return pa_decode_append(PA_DECODE_ARGS, stream, key, value);
+    }
+    if (!key || !value) return PA_ERR_NULL;
+    if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_SHAPE;
+    PA_CHECK_SEQUENCES();
+#if PA_CHECK_CONTENTS
+    const int cp = pa::check::pairs(block_pairs, num_pairs, num_blocks, num_blocks, true, (hipStream_t)stream);
+    if (cp != PA_OK) return cp;
+#endif
+    const hipStream_t s = (hipStream_t)stream;
+    pr.args.new_k = key;
+    pr.args.new_v = value;
+    pr.args.cow_pairs = block_pairs;
+    pr.args.cow_num = num_pairs;
     const int s1 = pa::run_partition(pr, s);
     if (s1 != PA_OK) return s1;
     return pa::run_reduce(pr, s);

@@ -132,9 +132,45 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     const int id_lim = min(min(P / BS, 64), a.max_blocks_per_seq - lb0);
     int ids = lane < id_lim ? bt[lane] : 0;
     const int T = a.seq_lens[seq];
+    // copy-on-write pairs of this launch (decode with append only), one per
+    // lane; -1 for lanes past them and for pairs outside the pool, which are
+    // skipped as by pa_copy_blocks
+    const bool cow = APPEND && a.cow_num > 0;
+    int cow_src = -1, cow_dst = -1;
+    if (cow && lane < a.cow_num) {
+        const int64_t s = a.cow_pairs[2 * lane];
+        const int64_t d = a.cow_pairs[2 * lane + 1];
+        const bool in_pool = s >= 0 && s < a.num_blocks && d >= 0 && d < a.num_blocks;
+        cow_src = in_pool ? (int)s : -1;
+        cow_dst = in_pool ? (int)d : -1;
+    }
     // wait for the ids here, together with the length: the compiler does not
     // see the asynchronous copies below and would otherwise wait for them too
-    asm volatile("" : "+v"(ids));
+    if constexpr (APPEND)
+        asm volatile("" : "+v"(ids), "+v"(cow_src), "+v"(cow_dst));
+    else
+        asm volatile("" : "+v"(ids));
+    // A block that a pair of this launch overwrites is read from the pair's
+    // source, which holds the same content once copied (the copying
+    // workgroups run beside this one).  When it is the sequence's last
+    // block, the copying workgroup also stores the new token into it, after
+    // its copy; this workgroup then stores nothing (moved).
+    int moved = 0;
+    if (cow) {
+        // four pairs per trip: j + u <= 63 while j < cow_num <= 64, and lanes
+        // past the pairs hold -1, which matches no id
+        static_assert(COW_MAX_PAIRS <= 64, "one pair per lane");
+        for (int j = 0; j < a.cow_num; j += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int d = __builtin_amdgcn_readlane(cow_dst, j + u);
+                const int sr = __builtin_amdgcn_readlane(cow_src, j + u);
+                const bool hit = d >= 0 && ids == d;
+                ids = hit ? sr : ids;
+                moved = hit ? 1 : moved;
+            }
+        }
+    }
     if (T <= 0 || T > a.max_seq_len) return;
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
     const int n_parts = (T + P - 1) / P;
@@ -313,14 +349,16 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
         if (k == 0) load_q();
         if (appends && k == nbw - 1) {
             // the host appends here only when a partition has at most 64 blocks
-            const int pb = __builtin_amdgcn_readlane(ids, min((nblk - 1) / HALVES, 63));
+            const int last = min((nblk - 1) / HALVES, 63);
+            const int pb = __builtin_amdgcn_readlane(ids, last);
+            const bool stores = __builtin_amdgcn_readlane(moved, last) == 0;  // else the copying workgroup does
             if (lane < NG) {
                 const u32x4 kg = *(const u32x4*)(new_lds + lane * 16);
                 const u32x4 vg = *(const u32x4*)(new_lds + ROWB + lane * 16);
                 char* row = ring + stage * Sh::STAGE + new_row * ROWB;
                 *(u32x4*)(row + ((lane ^ (new_row & (NG - 1))) * 16)) = kg;  // K granules are swizzled
                 *(u32x4*)(row + TILE + lane * 16) = vg;
-                if ((unsigned)pb < (unsigned)a.num_blocks) {
+                if (stores && (unsigned)pb < (unsigned)a.num_blocks) {
                     const size_t dst = ((size_t)pb * a.num_kv_heads + kvh) * POOL_TILE + ((T - 1) % BS) * ROWB + lane * 16;
                     *(u32x4*)((char*)a.k_cache + dst) = kg;
                     *(u32x4*)((char*)a.v_cache + dst) = vg;
@@ -392,10 +430,78 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     }
 }
 
+// Copy-on-write pair w / 2 of the launch, tensor w % 2 (K, then V): the
+// whole destination block (all kv heads, all rows) from the source block,
+// as pa_copy_blocks does.  When the destination is some sequence's last
+// block, that sequence's new token is then stored into it: the copy's
+// stores have completed by then, and the partition workgroups read the
+// source instead and store nothing there.  NT threads.
+template <Fmt KV, int D, int BS, int NT>
+__device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int ROW_G = D * FmtBytes<KV>::value / 16;  // 16-byte granules per row
+    const int p = (int)(w >> 1);
+    const int z = (int)(w & 1);
+    const int64_t src = a.cow_pairs[2 * p];
+    const int64_t dst = a.cow_pairs[2 * p + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;  // skipped pair
+    const int H = a.num_kv_heads;
+    const int granules = H * BS * ROW_G;  // one tensor's block
+    u32x4* pool = (u32x4*)(z == 0 ? a.k_cache : a.v_cache);
+    const u32x4* from = pool + (size_t)src * granules;
+    u32x4* to = pool + (size_t)dst * granules;
+    int* who = (int*)smem;  // the sequence whose last block is dst
+    if (threadIdx.x == 0) *who = -1;
+    // the first sequences' lengths are loaded with the copy
+    const int B = a.block_size;
+    const int s0 = (int)threadIdx.x;
+    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
+    constexpr int U = 4;
+    for (int i0 = (int)threadIdx.x; i0 < granules; i0 += U * NT) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * NT < granules) v[u] = from[i0 + u * NT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * NT < granules) to[i0 + u * NT] = v[u];
+    }
+    __syncthreads();  // who is initialised
+    for (int s = s0; s < a.num_seqs; s += NT) {
+        const int T = s == s0 ? T0 : a.seq_lens[s];
+        if (T > 0 && T <= a.max_seq_len && (T + B - 1) / B <= a.max_blocks_per_seq &&
+            a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / B] == (int)dst)
+            *who = s;  // one sequence for valid input (destinations belong to one sequence)
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's copy stores are complete
+    __syncthreads();
+    const int s = *who;
+    if (s < 0) return;
+    const int row = (a.seq_lens[s] - 1) % B;
+    const u32x4* tok = (const u32x4*)(z == 0 ? a.new_k : a.new_v) + (size_t)s * H * ROW_G;
+    for (int i = (int)threadIdx.x; i < H * ROW_G; i += NT) {
+        const int h = i / ROW_G;
+        const int g = i - h * ROW_G;
+        to[((size_t)h * BS + row) * ROW_G + g] = tok[i];
+    }
+}
+
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
 __global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
 decode_partition_gqa4_kernel(const DecodeArgs a) {
-    gqa4_partition<KV, D, BS, W, S, APPEND>(a, blockIdx.x);
+    if constexpr (APPEND) {
+        // decode with append: the copy-on-write pairs' workgroups come last,
+        // where the tail of the partition work leaves slots idle (nothing here
+        // reads their destinations)
+        const unsigned parts = (unsigned)a.num_seqs * (unsigned)a.max_partitions * (unsigned)a.num_kv_heads;
+        if (blockIdx.x >= parts) {
+            cow_copy_block<KV, D, BS, W * 64>(a, blockIdx.x - parts);
+            return;
+        }
+        gqa4_partition<KV, D, BS, W, S, APPEND>(a, blockIdx.x);
+    } else {
+        gqa4_partition<KV, D, BS, W, S, APPEND>(a, blockIdx.x);
+    }
 }
 
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
@@ -406,7 +512,8 @@ int launch_partition_gqa4_as(const DecodeArgs& a, hipStream_t stream) {
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
+    const size_t copies = APPEND ? 2 * (size_t)a.cow_num : 0;
+    const dim3 grid((unsigned)(copies + (size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

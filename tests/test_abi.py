@@ -245,6 +245,34 @@ def test_decode_append_validation(lib):
     assert _append(lib, value=FAKE + 4) == SHAPE
 
 
+def _cow(lib, pairs=FAKE, num_pairs=16, key=FAKE, value=FAKE, **kw):
+    a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, k_cache=FAKE, v_cache=FAKE, kv_dtype=BF16,
+             tables=FAKE, max_blocks=256, seq_lens=FAKE, max_seq_len=4096, num_seqs=64, heads=32, kv_heads=8,
+             dim=128, block=16, blocks=9000, scale=0.088, k_scale=None, v_scale=None, part=512, ws=FAKE,
+             ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.pa_decode_append_cow(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k_cache"], a["v_cache"],
+                                    a["kv_dtype"], a["tables"], a["max_blocks"], a["seq_lens"], a["max_seq_len"],
+                                    a["num_seqs"], a["heads"], a["kv_heads"], a["dim"], a["block"], a["blocks"],
+                                    ctypes.c_float(a["scale"]), a["k_scale"], a["v_scale"], a["part"], a["ws"],
+                                    a["ws_bytes"], None, key, value, pairs, num_pairs)
+
+
+def test_decode_append_cow_validation(lib):
+    # every case returns before any launch
+    assert _cow(lib, num_pairs=-1) == SHAPE
+    assert _cow(lib, pairs=None) == NULL
+    assert _cow(lib, pairs=None, num_pairs=0, num_seqs=0) == OK  # nothing to copy, nothing to decode
+    assert _cow(lib, q_dtype=F16) == DTYPE  # pa_decode's checks
+    assert _cow(lib, out=None) == NULL
+    need = lib.pa_decode_workspace_size(64, 32, 128, 4096, 512)
+    assert _cow(lib, ws_bytes=need - 1) == WS
+    # the one-launch shape (bf16, four query heads per kv head, 32 blocks per partition): the new rows
+    assert _cow(lib, key=None) == NULL
+    assert _cow(lib, value=None) == NULL
+    assert _cow(lib, key=FAKE + 8) == SHAPE  # misaligned
+
+
 def _sp(lib, gs=FAKE, gp=FAKE, groups=4, mgs=16, mpl=1024, **kw):
     a = dict(out=FAKE, out_dtype=F32, q=FAKE, q_dtype=BF16, k_cache=FAKE, v_cache=FAKE, kv_dtype=BF16,
              tables=FAKE, max_blocks=256, seq_lens=FAKE, max_seq_len=4096, num_seqs=64, heads=32, kv_heads=8,

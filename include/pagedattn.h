@@ -362,8 +362,8 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
  * copies run in the same launch: its last 2 num_pairs workgroups copy the
  * pairs (K and V), the partition workgroups read a destination block from
  * its source (the same content once copied), and when a destination is a
- * sequence's last block its copying workgroup stores that sequence's new
- * token into it after the copy.  Other shapes make the two calls.
+ * sequence's last block its copying workgroup writes that sequence's new
+ * token in place of the copied row.  Other shapes make the two calls.
  *   block_pairs  int64 [num_pairs][2] (source, destination), device; pairs
  *                outside the pool are skipped, as by pa_copy_blocks
  *   num_pairs    >= 0; 0 makes this pa_decode_append

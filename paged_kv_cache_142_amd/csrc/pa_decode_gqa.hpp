@@ -152,25 +152,18 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
         asm volatile("" : "+v"(ids));
     // A block that a pair of this launch overwrites is read from the pair's
     // source, which holds the same content once copied (the copying
-    // workgroups run beside this one).  When it is the sequence's last
-    // block, the copying workgroup also stores the new token into it, after
-    // its copy; this workgroup then stores nothing (moved).
-    int moved = 0;
-    if (cow) {
-        // four pairs per trip: j + u <= 63 while j < cow_num <= 64, and lanes
-        // past the pairs hold -1, which matches no id
-        static_assert(COW_MAX_PAIRS <= 64, "one pair per lane");
-        for (int j = 0; j < a.cow_num; j += 4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int d = __builtin_amdgcn_readlane(cow_dst, j + u);
-                const int sr = __builtin_amdgcn_readlane(cow_src, j + u);
-                const bool hit = d >= 0 && ids == d;
-                ids = hit ? sr : ids;
-                moved = hit ? 1 : moved;
-            }
+    // workgroups run beside this one).  Each block id is checked when its
+    // copy is issued (one compare of the pair lanes against it), so that
+    // nothing stands between the ids' arrival and the first copies.  When
+    // the sequence's last block is a destination, its copying workgroup
+    // writes the new token into it, and this workgroup stores nothing there.
+    auto source_of = [&](int pb) {
+        if (cow) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(cow_dst == pb);
+            if (hit != 0) pb = __builtin_amdgcn_readlane(cow_src, (int)__builtin_ctzll(hit));
         }
-    }
+        return pb;
+    };
     if (T <= 0 || T > a.max_seq_len) return;
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
     const int n_parts = (T + P - 1) / P;
@@ -241,6 +234,7 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
         // pending table load may still write would make later copies wait)
         int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : __builtin_amdgcn_readfirstlane(bt[idx]);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
+        pb = source_of(pb);
         size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * POOL_TILE;
         if constexpr (HALVES > 1) tile += (size_t)(vidx % HALVES) * TILE;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
@@ -351,7 +345,7 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
             // the host appends here only when a partition has at most 64 blocks
             const int last = min((nblk - 1) / HALVES, 63);
             const int pb = __builtin_amdgcn_readlane(ids, last);
-            const bool stores = __builtin_amdgcn_readlane(moved, last) == 0;  // else the copying workgroup does
+            const bool stores = source_of(pb) == pb;  // else the copying workgroup does
             if (lane < NG) {
                 const u32x4 kg = *(const u32x4*)(new_lds + lane * 16);
                 const u32x4 vg = *(const u32x4*)(new_lds + ROWB + lane * 16);
@@ -433,56 +427,74 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
 // Copy-on-write pair w / 2 of the launch, tensor w % 2 (K, then V): the
 // whole destination block (all kv heads, all rows) from the source block,
 // as pa_copy_blocks does.  When the destination is some sequence's last
-// block, that sequence's new token is then stored into it: the copy's
-// stores have completed by then, and the partition workgroups read the
-// source instead and store nothing there.  NT threads.
+// block, the row of that sequence's new token is written from the new token
+// instead of from the source (the partition workgroups read the source for
+// that block and store nothing there).  These workgroups are the last of the
+// launch, so their chain of dependent memory accesses is kept short: the
+// owner search (each sequence's length, then its last block id) runs beside
+// the copy's loads, and no store waits for another.  NT threads.
 template <Fmt KV, int D, int BS, int NT>
 __device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int ROW_G = D * FmtBytes<KV>::value / 16;  // 16-byte granules per row
+    constexpr int U = 8;                                 // granules per thread in flight
     const int p = (int)(w >> 1);
     const int z = (int)(w & 1);
+    const int s0 = (int)threadIdx.x;
+    // the first sequences' lengths, loaded with the pair
+    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
     const int64_t src = a.cow_pairs[2 * p];
     const int64_t dst = a.cow_pairs[2 * p + 1];
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;  // skipped pair
     const int H = a.num_kv_heads;
-    const int granules = H * BS * ROW_G;  // one tensor's block
+    const int granules = H * BS * ROW_G;  // one tensor's block: [kv head][row][granule]
     u32x4* pool = (u32x4*)(z == 0 ? a.k_cache : a.v_cache);
     const u32x4* from = pool + (size_t)src * granules;
     u32x4* to = pool + (size_t)dst * granules;
-    int* who = (int*)smem;  // the sequence whose last block is dst
-    if (threadIdx.x == 0) *who = -1;
-    // the first sequences' lengths are loaded with the copy
-    const int B = a.block_size;
-    const int s0 = (int)threadIdx.x;
-    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
-    constexpr int U = 4;
-    for (int i0 = (int)threadIdx.x; i0 < granules; i0 += U * NT) {
-        u32x4 v[U];
+    const u32x4* tok = (const u32x4*)(z == 0 ? a.new_k : a.new_v);  // [seq][kv head][granule]
+    int* who = (int*)smem;  // the sequence whose last block is dst, and its new token's row
+    if (threadIdx.x == 0) who[0] = -1;
+
+    u32x4 v[U];
+    auto load = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (i0 + u * NT < granules) v[u] = from[i0 + u * NT];
+    };
+    auto store = [&](int i0, int s, int row) {
+        // the new token's granules are loaded together, then everything is stored
+        u32x4 t[U];
+        bool take[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * NT;
+            take[u] = s >= 0 && i < granules && (i / ROW_G) % BS == row;
+            if (take[u]) t[u] = tok[((size_t)s * H + i / (BS * ROW_G)) * ROW_G + i % ROW_G];
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (i0 + u * NT < granules) to[i0 + u * NT] = v[u];
+            if (i0 + u * NT < granules) to[i0 + u * NT] = take[u] ? t[u] : v[u];
+    };
+    auto owns = [&](int s, int T) {
+        return T > 0 && T <= a.max_seq_len && (T + BS - 1) / BS <= a.max_blocks_per_seq &&
+               a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / BS] == (int)dst;
+    };
+    load(s0);
+    const bool mine = s0 < a.num_seqs && owns(s0, T0);
+    __syncthreads();  // who[0] is initialised
+    // one sequence for valid input (destinations belong to one sequence)
+    if (mine) { who[0] = s0; who[1] = (T0 - 1) % BS; }
+    for (int s = s0 + NT; s < a.num_seqs; s += NT) {
+        const int T = a.seq_lens[s];
+        if (owns(s, T)) { who[0] = s; who[1] = (T - 1) % BS; }
     }
-    __syncthreads();  // who is initialised
-    for (int s = s0; s < a.num_seqs; s += NT) {
-        const int T = s == s0 ? T0 : a.seq_lens[s];
-        if (T > 0 && T <= a.max_seq_len && (T + B - 1) / B <= a.max_blocks_per_seq &&
-            a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / B] == (int)dst)
-            *who = s;  // one sequence for valid input (destinations belong to one sequence)
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's copy stores are complete
     __syncthreads();
-    const int s = *who;
-    if (s < 0) return;
-    const int row = (a.seq_lens[s] - 1) % B;
-    const u32x4* tok = (const u32x4*)(z == 0 ? a.new_k : a.new_v) + (size_t)s * H * ROW_G;
-    for (int i = (int)threadIdx.x; i < H * ROW_G; i += NT) {
-        const int h = i / ROW_G;
-        const int g = i - h * ROW_G;
-        to[((size_t)h * BS + row) * ROW_G + g] = tok[i];
+    const int s = who[0];
+    const int row = s >= 0 ? who[1] : -1;
+    store(s0, s, row);
+    for (int i0 = s0 + U * NT; i0 < granules; i0 += U * NT) {
+        load(i0);
+        store(i0, s, row);
     }
 }
 

@@ -89,11 +89,10 @@ struct DecodeArgs {
     int cow_num;
 };
 
-// Pairs that one launch takes; more go through a launch of their own.  The
-// partition workgroups' check of their block ids costs each of them about a
-// pair's worth of instructions per pair, and the copying workgroups run in
-// the launch's tail: with 16 pairs the step was 1.5 us faster than with the
-// separate copy launch, with 40 pairs 2.8 us slower.
+// Pairs that one launch takes (one per lane of the partition workgroups'
+// check); more go through a launch of their own.  The copying workgroups run
+// in the launch's tail: with 16 pairs the step was 1.5 us faster than with
+// the separate copy launch, with 40 pairs 2.8 us slower.
 constexpr int COW_MAX_PAIRS = 16;
 
 constexpr int PLAN_ITEMS_OFFSET = 64;

@@ -391,35 +391,40 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     int bad = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) bad |= winv[w];
-    const float vs = 1.f;
-    for (int o = threadIdx.x; o < G * D; o += W * 64) {
-        const int g = o / D;
-        const int d = o - g * D;
+    // two consecutive dims per thread, so that each row leaves in 8-byte
+    // stores (merge_pos keeps pairs of dims together)
+    for (int o2 = threadIdx.x; o2 < G * D / 2; o2 += W * 64) {
+        const int g = o2 / (D / 2);
+        const int d0 = 2 * (o2 - g * (D / 2));
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + g]);
         const float mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f, A = 0.f;
+        float L = 0.f;
+        f32x2 A = {0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float f = fast_exp2(wm[w * G + g] - mu);
-            float rows = 0.f;
+            f32x2 rows = {0.f, 0.f};
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) rows += wacc[((w * R + rr) * G + g) * D + merge_pos(d)];
+            for (int rr = 0; rr < R; ++rr) rows += *(const f32x2*)(wacc + ((w * R + rr) * G + g) * D + merge_pos(d0));
             L = fmaf(f, wl[w * G + g], L);
-            A = fmaf(f, rows, A);
+            A[0] = fmaf(f, rows[0], A[0]);
+            A[1] = fmaf(f, rows[1], A[1]);
         }
         const int hq = hq0 + g;
         const size_t row = (size_t)seq * a.num_heads + hq;
+        const float nan = __builtin_nanf("");
         if (n_parts == 1) {
-            store_out(a.out, a.out_dtype, row * D + d, bad ? __builtin_nanf("") : A / L * vs);
+            store_out(a.out, a.out_dtype, row * D + d0, bad ? nan : A[0] / L);
+            store_out(a.out, a.out_dtype, row * D + d0 + 1, bad ? nan : A[1] / L);
         } else {
             const size_t pidx = row * a.max_partitions + part;
-            if (d == 0) {
-                store_state(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
-                store_state(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
+            if (d0 == 0) {
+                store_state(&a.part_m[pidx], bad ? nan : M);
+                store_state(&a.part_l[pidx], bad ? nan : L);
             }
-            store_state(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
+            *(f32x2*)(a.part_acc + pidx * D + d0) = bad ? f32x2{nan, nan} : A;
         }
     }
 }

@@ -454,9 +454,15 @@ decode_partition_kernel(const DecodeArgs a) {
         for (int g = 0; g < G; ++g) qop[g].pin();
     }
     float qk_scale = a.qk_scale_log2;
+    // The value scale is needed only by the final stores, but a load issued
+    // there would add a memory round trip to every workgroup's end; both
+    // scales are loaded here and made resident before the copies, like the
+    // queries.
+    float vs = 1.f;
     if constexpr (KV == Fmt::FP8) {
         float ks = a.k_scale[kvh];
-        asm volatile("" : "+v"(ks));  // resident before the copies, like the queries
+        vs = a.v_scale[kvh];
+        asm volatile("" : "+v"(ks), "+v"(vs));
         qk_scale *= ks;
     }
 
@@ -588,7 +594,6 @@ decode_partition_kernel(const DecodeArgs a) {
         }
     }
 
-    const float vs = KV == Fmt::FP8 ? a.v_scale[kvh] : 1.f;
     auto emit = [&](int g, int d, float M, float L, float A, int bad) {
         const int hq = hq0 + g;
         const size_t row = (size_t)seq * a.num_heads + hq;

@@ -143,6 +143,9 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     int ids = lane < id_lim ? bt[lane] : 0;
     const int T = a.seq_lens[seq];
     float k_scale = a.k_scale[kvh];
+    // the value scale is used only by the final stores; loaded here, with the
+    // ids, it adds no memory round trip to the workgroup's end
+    float vs = a.v_scale[kvh];
     // Query operand: head n's elements 32 g .. 32 g + 31 (zero for n >= G).
     bf16x8 qop[Sh::NC];
     {
@@ -157,7 +160,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     }
     // make ids and queries resident before any asynchronous copy is queued:
     // the compiler does not see those copies and would otherwise wait for them
-    asm volatile("" : "+v"(ids), "+v"(k_scale));
+    asm volatile("" : "+v"(ids), "+v"(k_scale), "+v"(vs));
 #pragma unroll
     for (int c = 0; c < Sh::NC; ++c) asm volatile("" : "+v"(qop[c]));
     if (T <= 0 || T > a.max_seq_len) return;
@@ -368,32 +371,41 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     int bad = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) bad |= winv[w];
-    const float vs = a.v_scale[kvh];
     const int hq0 = kvh * G;
-    for (int o = threadIdx.x; o < G * D; o += W * 64) {
-        const int hg = o / D;
-        const int d = o - hg * D;
+    // four consecutive dims per thread, so that each state row leaves in
+    // 16-byte stores (granule x of head hg's row sits at x ^ hg)
+    for (int o4 = threadIdx.x; o4 < G * D / 4; o4 += W * 64) {
+        const int hg = o4 / (D / 4);
+        const int d0 = 4 * (o4 - hg * (D / 4));
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + hg]);
         const float mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f, A = 0.f;
+        float L = 0.f;
+        f32x4 A = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float f = fast_exp2(wm[w * G + hg] - mu);
             L = fmaf(f, wl[w * G + hg], L);
-            A = fmaf(f, wacc[(w * G + hg) * D + (d ^ (hg << 2))], A);
+            const f32x4 v = *(const f32x4*)(wacc + (w * G + hg) * D + (d0 ^ (hg << 2)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) A[e] = fmaf(f, v[e], A[e]);
         }
         const size_t row = (size_t)seq * a.num_heads + hq0 + hg;
+        const float nan = __builtin_nanf("");
         if (n_parts == 1) {
-            store_out(a.out, a.out_dtype, row * D + d, bad ? __builtin_nanf("") : A / L * vs);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, row * D + d0 + e, bad ? nan : A[e] / L * vs);
         } else {
             const size_t pidx = row * a.max_partitions + part;
-            if (d == 0) {
-                store_state_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
-                store_state_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
+            if (d0 == 0) {
+                store_state_stream(&a.part_m[pidx], bad ? nan : M);
+                store_state_stream(&a.part_l[pidx], bad ? nan : L);
             }
-            store_state_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
+            f32x4 st;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[e] = bad ? nan : A[e] * vs;
+            __builtin_nontemporal_store(st, (f32x4*)(a.part_acc + pidx * D + d0));
         }
     }
 }

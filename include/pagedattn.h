@@ -200,7 +200,11 @@ int pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_
  *
  * Holds one partial state (m, l, acc[head_dim]) in float32 per (sequence,
  * query head, KV partition), with ceil(max_seq_len / partition_size)
- * partitions per sequence.  Returns 0 for invalid arguments.
+ * partitions per sequence: acc in rows of head_dim; m and l in 64-byte
+ * records of one kv head's group, each written whole (sized for one record
+ * per query head, the most kv heads there can be), or in per-row arrays
+ * inside the same space for groups of four query heads over 16-bit K/V.  Its
+ * contents need no initialisation.  Returns 0 for invalid arguments.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_seq_len,
                                 int partition_size);

@@ -15,13 +15,16 @@ static int num_partitions(int max_seq_len, int partition_size) {
     return (max_seq_len + partition_size - 1) / partition_size;
 }
 
-// Workspace: m[N][H][P_max] | l[N][H][P_max] | acc[N][H][P_max][D] (float32)
-// | plan (int32: count, then N * P_max work items) | skipped partitions per
-// sequence (int32 [N], shared-prefix decode), each part starting on a
-// 256-byte boundary.
+// Workspace: m and l | acc[N][H][P_max][D] (float32) | plan (int32: count,
+// then N * P_max work items) | skipped partitions per sequence (int32 [N],
+// shared-prefix decode), each part starting on a 256-byte boundary.  m and l
+// are either records (ML_REC float32 per (sequence, kv head, partition),
+// sized for N * H * P_max, the most kv heads there can be) or, for calls
+// whose partition kernel is the GQA-4 one, m[N][H][P_max] then l[N][H][P_max]
+// (256-byte aligned) inside the same area.
 static size_t plan_offset(int num_seqs, int num_heads, int head_dim, int max_parts) {
     const size_t rows = (size_t)num_seqs * num_heads * max_parts;
-    return 2 * align256(rows * 4) + align256(rows * head_dim * 4);
+    return align256(rows * ML_REC * 4) + align256(rows * head_dim * 4);
 }
 static size_t skip_offset(int num_seqs, int num_heads, int head_dim, int max_parts) {
     return plan_offset(num_seqs, num_heads, head_dim, max_parts) +
@@ -147,8 +150,13 @@ __global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const Dec
     const int n_parts = (!in_grid || bad || T == 0) ? 0 : (T + a.partition_size - 1) / a.partition_size;
     const bool merge = n_parts > 1;
     const size_t base = row * a.max_partitions;
-    const float* pm = a.part_m + base;
-    const float* pl = a.part_l + base;
+    // m and l of partition p: pm[p * ms], pl[p * ms]
+    const int hq = in_grid ? (int)(row - (size_t)seq * a.num_heads) : 0;
+    const int G = a.num_heads / a.num_kv_heads;
+    const int kvh = hq / G;
+    const int ms = a.ml_records ? ML_REC : 1;  // stride between partitions
+    const float* pm = a.ml_records ? a.part_ml + ml_record(a, seq, kvh, 0) + (hq - kvh * G) : a.part_m + base;
+    const float* pl = a.ml_records ? pm + ML_L : a.part_l + base;
     const float4* pacc = (const float4*)(a.part_acc + base * D) + c4;
 
     float mv[U], lv[U];
@@ -158,8 +166,8 @@ __global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const Dec
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u * RG;
             const bool have = merge && p < n_parts;
-            mv[u] = have ? pm[p] : -INFINITY;
-            lv[u] = have ? pl[p] : 0.f;
+            mv[u] = have ? pm[(size_t)p * ms] : -INFINITY;
+            lv[u] = have ? pl[(size_t)p * ms] : 0.f;
             av[u] = have ? pacc[(size_t)p * C4] : float4{0.f, 0.f, 0.f, 0.f};
         }
     };
@@ -181,7 +189,7 @@ __global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const Dec
     float mx = mv[0];
 #pragma unroll
     for (int u = 1; u < U; ++u) mx = fmaxf(mx, mv[u]);
-    for (int p = pg + RG * U; merge && p < n_parts; p += RG) mx = fmaxf(mx, pm[p]);
+    for (int p = pg + RG * U; merge && p < n_parts; p += RG) mx = fmaxf(mx, pm[(size_t)p * ms]);
     if (c4 == 0) red_m[rw][pg] = mx;
     __syncthreads();
     float M = red_m[rw][0];
@@ -230,9 +238,10 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Point the partition states and the plan into a workspace laid out as
 // workspace_bytes_for describes (rows = N * H * P_max state rows).
 static void bind_workspace(DecodeArgs& a, void* workspace, size_t rows, size_t plan_at) {
+    a.part_ml = (float*)workspace;
     a.part_m = (float*)workspace;
     a.part_l = (float*)((char*)workspace + align256(rows * 4));
-    a.part_acc = (float*)((char*)workspace + 2 * align256(rows * 4));
+    a.part_acc = (float*)((char*)workspace + align256(rows * ML_REC * 4));
     a.plan = (int*)((char*)workspace + plan_at);
 }
 
@@ -310,6 +319,7 @@ static int prepare(Prepared& pr, void* out, int out_dtype, const void* q, int q_
     a.max_partitions = max_parts;
     bind_workspace(a, workspace, rows, plan_offset(num_seqs, num_heads, head_dim, max_parts));
     a.inline_plan = num_seqs <= INLINE_PLAN_MAX_SEQS && partition_size / block_size <= INLINE_PLAN_MAX_BLOCKS;
+    a.ml_records = partition_kernel_is_gqa4(kv_dtype, group) ? 0 : 1;
     a.skip_parts = nullptr;
     a.new_k = nullptr;
     a.cow_pairs = nullptr;

@@ -60,8 +60,16 @@ struct DecodeArgs {
     const float* v_scale;
     int partition_size;
     int max_partitions;
-    float* part_m;    // [num_seqs][num_heads][max_partitions]
-    float* part_l;    // [num_seqs][num_heads][max_partitions]
+    // m and l of the partition states, in one of two layouts over the same
+    // workspace area, chosen per call (every kernel of a call uses its layout):
+    // ml_records = 1: records of ML_REC floats, one per (sequence, kv head,
+    // partition), [num_seqs][num_kv_heads][max_partitions] at part_ml;
+    // ml_records = 0: part_m and part_l, [num_seqs][num_heads][max_partitions]
+    // each (the GQA-4 kernel, whose few states read faster this way).
+    int ml_records;
+    float* part_ml;
+    float* part_m;
+    float* part_l;
     float* part_acc;  // [num_seqs][num_heads][max_partitions][head_dim]
     // Work order written by the plan kernel: plan[0] = number of (sequence,
     // partition) items, plan[PLAN_ITEMS_OFFSET + k] = seq * max_partitions +
@@ -96,6 +104,55 @@ struct DecodeArgs {
 constexpr int COW_MAX_PAIRS = 16;
 
 constexpr int PLAN_ITEMS_OFFSET = 64;
+
+// Partition-state record of m and l: m of head g of the kv head's group at
+// [g], l at [ML_L + g], the rest zero; 64 bytes on a 64-byte boundary.
+// Kernels that compute a whole group write it with one 16-lane store, so that
+// it reaches memory whole: scattered 4-byte stores of m and l, partial writes
+// among the K/V reads, cost the long-context FP8 partition launch 4.3% (a
+// timing-only variant without them); 64- and 128-byte records measured the
+// same.
+constexpr int ML_REC = 16;
+constexpr int ML_L = 8;
+
+// Whether a call's partition kernel is the GQA-4 one (groups of four query
+// heads over 16-bit K/V; the per-format dispatch makes the same choice).  Its
+// calls keep m and l in per-row arrays (ml_records = 0): on the gqa workload
+// the reduce read the records 0.6 us slower than the arrays, while the
+// kernel itself gained nothing from them.  Every other partition kernel
+// writes records.
+inline bool partition_kernel_is_gqa4(int kv_dtype, int group) {
+#ifdef PA_DISABLE_GQA4
+    (void)kv_dtype;
+    (void)group;
+    return false;
+#else
+    return group == 4 && (kv_dtype == PA_DTYPE_BF16 || kv_dtype == PA_DTYPE_F16);
+#endif
+}
+__device__ __forceinline__ size_t ml_record(const DecodeArgs& a, int seq, int kvh, int part) {
+    return (((size_t)seq * a.num_kv_heads + kvh) * a.max_partitions + part) * ML_REC;
+}
+
+// Lanes 0..ML_REC-1 of one wave store a record: lane j's value is m of head j (j <
+// G), l of head j - ML_L (ML_L <= j < ML_L + G), zero otherwise; NaN in place
+// of m and l when bad.  m_of(g) and l_of(g) give head g's values; each lane
+// evaluates only the one its element needs (g differs between lanes).  Every
+// lane of the wave may call it; only lanes below ML_REC store.
+template <int G, bool STREAM, typename MOf, typename LOf>
+__device__ __forceinline__ void store_ml_record(float* rec, int lane, bool bad, MOf m_of, LOf l_of) {
+    static_assert(G <= ML_L, "a record holds at most ML_L heads");
+    const bool is_l = lane >= ML_L;
+    const int g = is_l ? lane - ML_L : lane;
+    float v = 0.f;
+    if (g < G) v = bad ? __builtin_nanf("") : (is_l ? l_of(g) : m_of(g));
+    if (lane < ML_REC) {
+        if constexpr (STREAM)
+            __builtin_nontemporal_store(v, rec + lane);
+        else
+            rec[lane] = v;
+    }
+}
 constexpr int INLINE_PLAN_MAX_SEQS = 64;
 constexpr int INLINE_PLAN_MAX_BLOCKS = 64;
 
@@ -594,27 +651,35 @@ decode_partition_kernel(const DecodeArgs a) {
         }
     }
 
-    auto emit = [&](int g, int d, float M, float L, float A, int bad) {
+    auto emit = [&](int g, int d, float L, float A, int bad) {
         const int hq = hq0 + g;
         const size_t row = (size_t)seq * a.num_heads + hq;
         if (n_parts == 1) {
             store_out(a.out, a.out_dtype, row * D + d, bad ? __builtin_nanf("") : A / L * vs);
         } else {
             const size_t pidx = row * a.max_partitions + part;
-            if (d == 0) {
-                store_state_stream(&a.part_m[pidx], bad ? __builtin_nanf("") : M);
-                store_state_stream(&a.part_l[pidx], bad ? __builtin_nanf("") : L);
-            }
             store_state_stream(&a.part_acc[pidx * D + d], bad ? __builtin_nanf("") : A * vs);
         }
     };
+    float* const ml_rec = a.part_ml + ml_record(a, seq, kvh, part);
 
     if constexpr (W == 1) {
+        // lane 0's m and l, the values its rows' accumulators were merged with
+        auto lane0 = [](float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)); };
+        auto pick = [&](const float (&x)[G], int g) {  // x[g] of lane 0, g per lane
+            float r = lane0(x[0]);
+#pragma unroll
+            for (int gg = 1; gg < G; ++gg) r = g == gg ? lane0(x[gg]) : r;
+            return r;
+        };
+        if (n_parts > 1)
+            store_ml_record<G, true>(ml_rec, lane, invalid != 0, [&](int g) { return pick(m, g); },
+                                     [&](int g) { return pick(l, g); });
         if (r == 0) {
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) emit(g, Row::dim(c, e), m[g], l[g], acc[g][e], invalid);
+                for (int e = 0; e < 8; ++e) emit(g, Row::dim(c, e), l[g], acc[g][e], invalid);
         }
     } else {
         __syncthreads();  // every wave is done with its ring; reuse the LDS for the merge
@@ -639,12 +704,25 @@ decode_partition_kernel(const DecodeArgs a) {
         int bad = 0;
 #pragma unroll
         for (int w = 0; w < W; ++w) bad |= winv[w];
-        for (int o = threadIdx.x; o < G * D; o += W * 64) {
-            const int g = o / D;
-            const int d = o - g * D;
+        auto merged_m = [&](int g) {
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + g]);
+            return M;
+        };
+        auto merged_l = [&](int g) {
+            const float M = merged_m(g);
+            const float mu = M == -INFINITY ? 0.f : M;
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) L = fmaf(fast_exp2(wm[w * G + g] - mu), wl[w * G + g], L);
+            return L;
+        };
+        if (n_parts > 1 && wave == 0) store_ml_record<G, true>(ml_rec, lane, bad != 0, merged_m, merged_l);
+        for (int o = threadIdx.x; o < G * D; o += W * 64) {
+            const int g = o / D;
+            const int d = o - g * D;
+            const float M = merged_m(g);
             const float mu = M == -INFINITY ? 0.f : M;
             float L = 0.f, A = 0.f;
 #pragma unroll
@@ -653,7 +731,7 @@ decode_partition_kernel(const DecodeArgs a) {
                 L = fmaf(f, wl[w * G + g], L);
                 A = fmaf(f, wacc[(w * G + g) * D + merge_pos(d)], A);
             }
-            emit(g, d, M, L, A, bad);
+            emit(g, d, L, A, bad);
         }
     }
 }

@@ -372,14 +372,29 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < W; ++w) bad |= winv[w];
     const int hq0 = kvh * G;
+    auto merged_m = [&](int hg) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + hg]);
+        return M;
+    };
+    if (n_parts > 1 && wave == 0) {
+        auto merged_l = [&](int hg) {
+            const float M = merged_m(hg);
+            const float mu = M == -INFINITY ? 0.f : M;
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) L = fmaf(fast_exp2(wm[w * G + hg] - mu), wl[w * G + hg], L);
+            return L;
+        };
+        store_ml_record<G, true>(a.part_ml + ml_record(a, seq, kvh, part), lane, bad != 0, merged_m, merged_l);
+    }
     // four consecutive dims per thread, so that each state row leaves in
     // 16-byte stores (granule x of head hg's row sits at x ^ hg)
     for (int o4 = threadIdx.x; o4 < G * D / 4; o4 += W * 64) {
         const int hg = o4 / (D / 4);
         const int d0 = 4 * (o4 - hg * (D / 4));
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, wm[w * G + hg]);
+        const float M = merged_m(hg);
         const float mu = M == -INFINITY ? 0.f : M;
         float L = 0.f;
         f32x4 A = {0.f, 0.f, 0.f, 0.f};
@@ -398,10 +413,6 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
             for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, row * D + d0 + e, bad ? nan : A[e] / L * vs);
         } else {
             const size_t pidx = row * a.max_partitions + part;
-            if (d0 == 0) {
-                store_state_stream(&a.part_m[pidx], bad ? nan : M);
-                store_state_stream(&a.part_l[pidx], bad ? nan : L);
-            }
             f32x4 st;
 #pragma unroll
             for (int e = 0; e < 4; ++e) st[e] = bad ? nan : A[e] * vs;

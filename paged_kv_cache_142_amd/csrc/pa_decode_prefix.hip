@@ -184,9 +184,15 @@ __device__ __forceinline__ void prefix_states(const PrefixArgs& a, unsigned bid)
         return;
     }
     const size_t pidx = row * d.max_partitions + part;
-    if (g == 0) {
-        __builtin_nontemporal_store(bad ? nan : m, &d.part_m[pidx]);
-        __builtin_nontemporal_store(bad ? nan : l, &d.part_l[pidx]);
+    if (g == 0) {  // the column's m and l, in the call's layout
+        float* pm = d.part_m + pidx;
+        float* pl = d.part_l + pidx;
+        if (d.ml_records) {
+            pm = d.part_ml + ml_record(d, seq, kvh, part) + (head - kvh * G);
+            pl = pm + ML_L;
+        }
+        __builtin_nontemporal_store(bad ? nan : m, pm);
+        __builtin_nontemporal_store(bad ? nan : l, pl);
     }
     const float one = bad ? nan : 1.f;
 #pragma unroll

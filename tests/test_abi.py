@@ -46,16 +46,17 @@ def test_status_strings(lib):
 
 
 def test_workspace_size_formula(lib):
-    # m, l, acc[N][H][P][D] float32 arrays, each padded to 256 bytes, then the
+    # m/l records (16 float32 each, one per (sequence, head, partition) at
+    # most) and acc[N][H][P][D] float32, each padded to 256 bytes, then the
     # work plan: 64 header ints and one int per (sequence, partition), padded
     # too; then one int per sequence (partitions a shared prefix covers)
     n, h, d, msl, p = 64, 32, 128, 4096, 512
     parts = 8
     rows = n * h * parts
     pad = lambda x: (x + 255) // 256 * 256
-    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == (2 * pad(rows * 4) + pad(rows * d * 4)
+    assert lib.pa_decode_workspace_size(n, h, d, msl, p) == (pad(rows * 64) + pad(rows * d * 4)
                                                              + pad(4 * (64 + n * parts)) + 4 * n)
-    assert lib.pa_decode_workspace_size(3, 2, 64, 100, 16) == (2 * pad(3 * 2 * 7 * 4) + pad(3 * 2 * 7 * 64 * 4)
+    assert lib.pa_decode_workspace_size(3, 2, 64, 100, 16) == (pad(3 * 2 * 7 * 64) + pad(3 * 2 * 7 * 64 * 4)
                                                               + pad(4 * (64 + 3 * 7)) + 4 * 3)
     assert lib.pa_decode_workspace_size(1, 1, 64, 0, 16) == 256 + 4
     assert lib.pa_decode_workspace_size(-1, 1, 64, 10, 16) == 0

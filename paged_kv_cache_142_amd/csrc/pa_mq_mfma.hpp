@@ -153,10 +153,10 @@ __device__ __forceinline__ float mq_sum_groups(float x) {
 
 // D: head_dim; BS: block size; G: query heads per kv head; CB: 16-column
 // blocks per wave; STAGES: LDS ring depth.
-template <int D, int BS, int G, int CB = 1, int STAGES = PA_MQ_STAGES>
+template <int D, int BS, int G, int CB = 1, int STAGES = PA_MQ_STAGES, int WAVES = 4>
 struct MqShape {
     static constexpr int S = STAGES;              // LDS stages (S - 1 steps of copies in flight)
-    static constexpr int W = 4;                   // waves per workgroup
+    static constexpr int W = WAVES;               // waves per workgroup
     static constexpr int COLS = 16 * CB;          // query columns per wave
     static constexpr int TQ = W * COLS / G;       // query tokens (or sequences) per workgroup
     static constexpr int PER_WAVE = COLS / G;     // query tokens (or sequences) per wave
@@ -169,7 +169,7 @@ struct MqShape {
     static constexpr int COPIES_PER_WAVE = COPIES / W;
     static constexpr int ID_CAP = 2048;           // block ids held in LDS
     static constexpr int IDS_AT = S * STAGE;
-    static constexpr int LDS = IDS_AT + ID_CAP * 4 + 16;
+    static constexpr int LDS = IDS_AT + ID_CAP * 4 + (W * 4 + 15) / 16 * 16;
     static_assert(D == 128, "the lane roles assume head_dim 128");
     static_assert(BS == 16 || BS == 32, "block size");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
@@ -177,7 +177,7 @@ struct MqShape {
     static_assert(COPIES % W == 0 && COPIES / 2 % COPIES_PER_WAVE == 0, "a wave copies only K or only V");
     static_assert(BS % (4 * COPIES_PER_WAVE) == 0, "a wave's copies of one step stay inside one block");
     static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(W * 4 <= 16, "one bad-id flag per wave after the ids");
+
     static_assert(ID_CAP % BPS == 0, "a step's blocks never straddle an id window");
     static_assert(S >= 3, "two resident steps (the pipelined loop) plus one being refilled");
     static_assert((S - 2) * COPIES_PER_WAVE <= 63, "vmcnt holds the copies of S - 2 steps");
@@ -252,10 +252,10 @@ struct MqTask {
 // decode kernels' sense; `bad` is set when the table named a block outside
 // the pool.  All threads of the workgroup must call it.  STREAM marks the
 // K/V copies non-temporal (data read once).
-template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM, bool SPLIT>
+template <Fmt KV, int D, int BS, int G, int CB, int STAGES, bool STREAM, bool SPLIT, int WAVES = 4>
 __device__ void mq_tile(const MqPool& pool, const MqTask<CB>& t, char* smem, float (&m)[CB], float (&l)[CB],
                         f32x4 (&acc)[CB][2][4], bool& bad) {
-    using Sh = MqShape<D, BS, G, CB, STAGES>;
+    using Sh = MqShape<D, BS, G, CB, STAGES, WAVES>;
     using Ops = MfmaOps<KV>;
     using vec = typename Ops::vec;
     constexpr int ROWB = Sh::ROWB, STEP = Sh::STEP, BPS = Sh::BPS, S = Sh::S, CPW = Sh::COPIES_PER_WAVE;

@@ -127,9 +127,12 @@ __device__ bool prefill_item(const PrefillArgs& a, int p, int& seq, int& tile, P
     return false;
 }
 
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
 template <Fmt KV, int D, int BS, int G>
-__global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs a) {
-    using Sh = MqShape<D, BS, G, PREFILL_CB>;
+__global__ void __launch_bounds__(PA_PREFILL_WAVES * 64, 8 / PA_PREFILL_WAVES) prefill_mfma_kernel(const PrefillArgs a) {
+    using Sh = MqShape<D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
@@ -151,7 +154,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     const bool bad_seq = T <= 0 || T > a.max_seq_len || Q > T ||
                          (T + BS - 1) / BS > a.max_blocks_per_seq;
     if (bad_seq) {  // NaN rows for this tile
-        for (int o = threadIdx.x; o < (tok_hi - tok_lo) * G * D; o += 256) {
+        for (int o = threadIdx.x; o < (tok_hi - tok_lo) * G * D; o += Sh::W * 64) {
             const int tk = o / (G * D);
             const int rr = o - tk * G * D;
             const size_t row = (size_t)(q0 + tok_lo + tk) * a.num_heads + kvh * G + rr / D;
@@ -187,7 +190,8 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
     float m[PREFILL_CB], l[PREFILL_CB];
     f32x4 acc[PREFILL_CB][2][4];
     bool bad;
-    mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM, PA_PREFILL_SPLIT>(a.pool, t, smem, m, l, acc, bad);
+    mq_tile<KV, D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_STREAM, PA_PREFILL_SPLIT, PA_PREFILL_WAVES>(a.pool, t, smem, m,
+                                                                                                    l, acc, bad);
 
     // ---- output: column n of each block, dims 64 a + 16 b + 4 g + i, four
     // consecutive dims (i = 0..3) per store
@@ -206,7 +210,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(const PrefillArgs 
 
 template <Fmt KV, int D, int BS, int G>
 static int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    using Sh = MqShape<D, BS, G, PREFILL_CB>;
+    using Sh = MqShape<D, BS, G, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>;
     auto kernel = prefill_mfma_kernel<KV, D, BS, G>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
@@ -215,7 +219,7 @@ static int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const size_t items = (size_t)(a.total_q + Sh::TQ - 1) / Sh::TQ + (size_t)a.num_seqs;
     const size_t grid = items * a.pool.num_kv_heads;
     if (grid == 0) return PA_OK;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), Sh::LDS, stream, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(Sh::W * 64), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -223,10 +227,10 @@ template <Fmt KV, int D, int BS>
 static int dispatch_prefill_group(PrefillArgs& a, int group, int max_query_len, hipStream_t stream) {
     auto tiles = [&](int tq) { return (max_query_len + tq - 1) / tq; };
     switch (group) {
-        case 1: a.tiles = tiles(MqShape<D, BS, 1, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 1>(a, stream);
-        case 2: a.tiles = tiles(MqShape<D, BS, 2, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 2>(a, stream);
-        case 4: a.tiles = tiles(MqShape<D, BS, 4, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 4>(a, stream);
-        case 8: a.tiles = tiles(MqShape<D, BS, 8, PREFILL_CB>::TQ); return launch_prefill<KV, D, BS, 8>(a, stream);
+        case 1: a.tiles = tiles(MqShape<D, BS, 1, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>::TQ); return launch_prefill<KV, D, BS, 1>(a, stream);
+        case 2: a.tiles = tiles(MqShape<D, BS, 2, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>::TQ); return launch_prefill<KV, D, BS, 2>(a, stream);
+        case 4: a.tiles = tiles(MqShape<D, BS, 4, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>::TQ); return launch_prefill<KV, D, BS, 4>(a, stream);
+        case 8: a.tiles = tiles(MqShape<D, BS, 8, PREFILL_CB, PA_MQ_STAGES, PA_PREFILL_WAVES>::TQ); return launch_prefill<KV, D, BS, 8>(a, stream);
     }
     return PA_ERR_UNSUPPORTED;
 }

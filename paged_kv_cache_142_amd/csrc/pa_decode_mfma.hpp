@@ -387,7 +387,9 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
             for (int w = 0; w < W; ++w) L = fmaf(fast_exp2(wm[w * G + hg] - mu), wl[w * G + hg], L);
             return L;
         };
-        store_ml_record<G, true>(a.part_ml + ml_record(a, seq, kvh, part), lane, bad != 0, merged_m, merged_l);
+        // ordinary stores: 1.2% faster than non-temporal ones for the
+        // records (long_fp8), the opposite of the acc rows below
+        store_ml_record<G, false>(a.part_ml + ml_record(a, seq, kvh, part), lane, bad != 0, merged_m, merged_l);
     }
     // four consecutive dims per thread, so that each state row leaves in
     // 16-byte stores (granule x of head hg's row sits at x ^ hg)

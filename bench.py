@@ -802,8 +802,8 @@ def main():
         "step_mode": "hip_graph" if graph is not None else "eager",
         "step_calls": ((["pa_copy_blocks", "pa_decode_shared_prefix (with the new tokens)"] if groups is not None
                         else ["pa_copy_blocks", "pa_decode_append"] if dev.separate_cow
-                        else ["pa_decode_append_cow (the copies in the decode launch for four query heads per kv "
-                              "head; otherwise pa_copy_blocks, then pa_decode_append)"]) if dev.append_fused else
+                        else ["pa_decode_append_cow (the copies and the new tokens' store in the decode launch, "
+                              "but for the FP8 matrix-core shape: there pa_copy_blocks, then pa_decode_append)"]) if dev.append_fused else
                        ["pa_reshape_and_cache" + ("_fp8" if dev.quantize_step else ""), "pa_copy_blocks",
                         "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
                         *([] if groups is not None else ["pa_decode_reduce"])]),

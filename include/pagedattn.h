@@ -328,12 +328,13 @@ int pa_decode_reduce(void* out, int out_dtype, const void* q, int q_dtype, const
  * pa_decode computes.  The result and the pool are bitwise those of
  * pa_reshape_and_cache followed by pa_decode.
  *
- * For the GQA-4 kernel's shapes (bf16 or f16 K/V, four query heads per kv
- * head, at most 64 blocks per partition) the store happens inside the
- * partition kernel: the workgroup that
- * owns a sequence's last partition copies the new rows into the pool and
- * into its staged tile, saving the separate scatter launch.  Other shapes
- * launch a small copy kernel first.
+ * The store happens inside the partition kernel -- the wave that stages a
+ * sequence's last block writes the new rows into the pool and into its
+ * staged tile, saving the separate scatter launch -- for every shape but
+ * two: the FP8 matrix-core shape (E4M3 K/V, eight query heads per kv head,
+ * head_dim 128) and the GQA-4 shapes (bf16 or f16 K/V, four query heads per
+ * kv head) with more than 64 blocks per partition.  Those launch a small
+ * copy kernel first.
  *   key, value   [num_seqs][num_kv_heads][head_dim] in kv_dtype (for FP8
  *                pools, E4M3 codes), 16-byte aligned, device
  *   other arguments: as for pa_decode.  The block that holds position T - 1
@@ -360,20 +361,29 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
  * those of pa_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, ...)
  * followed by pa_decode_append with the same arguments.
  *
- * Where pa_decode_append stores the tokens inside the GQA-4 partition kernel
- * (bf16 or f16 K/V, four query heads per kv head, head_dim 64 or 128, block
- * size 16 or 32, at most 64 blocks per partition) and num_pairs <= 16, the
- * copies run in the same launch: its last 2 num_pairs workgroups copy the
- * pairs (K and V), the partition workgroups read a destination block from
- * its source (the same content once copied), and when a destination is a
- * sequence's last block its copying workgroup writes that sequence's new
- * token in place of the copied row.  Other shapes make the two calls.
+ * Where pa_decode_append stores the tokens inside the partition kernel
+ * (above; head_dim 64 or 128, block size 16 or 32) and num_pairs <= 16, the
+ * copies run in the same launch: its last workgroups copy the pairs (K and
+ * V, each block split into chunks of at most 8 16-byte granules per
+ * thread), the partition workgroups read a destination block from its
+ * source (the same content once copied), and when a destination is a
+ * sequence's last block its copying workgroups write that sequence's new
+ * token in place of the copied row.  Other shapes and more pairs make the
+ * two calls.
  *   block_pairs  int64 [num_pairs][2] (source, destination), device; pairs
  *                outside the pool are skipped, as by pa_copy_blocks
  *   num_pairs    >= 0; 0 makes this pa_decode_append
  *   other arguments: as for pa_decode_append.  Preconditions of
  *                pa_copy_blocks: destinations are distinct and none is a
  *                source; a destination belongs to at most one sequence.
+ *                And a source that is some sequence's last block (which
+ *                receives that sequence's token in this call) is copied only
+ *                to the last block of a sequence appending at the same row
+ *                (the copy-on-write of a shared last block before an
+ *                append): the one-launch path copies beside the tokens'
+ *                stores, so such a source may be read with or without its
+ *                token, and only then does the copy hold the right one (the
+ *                appending sequence's own).
  * Errors: PA_ERR_SHAPE for num_pairs < 0, PA_ERR_NULL for a null block_pairs
  * with num_pairs > 0, otherwise those of the two calls.
  */

@@ -137,6 +137,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
+// A wave-uniform read of memory that no workgroup of the launch writes
+// (lengths, the work order, scales), through the constant address space: the
+// compiler then reads it with a scalar load even in a kernel that stores to
+// other global memory, where it cannot prove the two apart and would issue a
+// vector load and a wait for it instead.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -382,16 +382,17 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(const u32x4* __restr
     }
 }
 
-// Shapes whose partition kernel stores the new tokens itself: the GQA-4
-// kernel, when a partition has at most 64 blocks (their ids sit in one
-// vector register).
+// Shapes whose partition kernel stores the new tokens itself (and takes the
+// launch's copy-on-write pairs): the GQA-4 kernel when a partition has at
+// most 64 blocks (their ids sit in one vector register), and the generic
+// kernel.  The FP8 matrix-core kernel does not.
 static bool partition_appends(const Prepared& pr) {
-#ifdef PA_DISABLE_GQA4
-    return false;
-#else
-    return (pr.kv_dtype == PA_DTYPE_BF16 || pr.kv_dtype == PA_DTYPE_F16) && pr.group == 4 &&
-           pr.args.partition_size / pr.args.block_size <= 64;
+    if (partition_kernel_is_gqa4(pr.kv_dtype, pr.group))
+        return pr.args.partition_size / pr.args.block_size <= 64;
+#ifndef PA_DISABLE_MFMA8
+    if (pr.kv_dtype == PA_DTYPE_FP8_E4M3 && pr.group == 8 && pr.head_dim == 128) return false;
 #endif
+    return true;
 }
 
 static int run_reduce(const Prepared& pr, hipStream_t stream) {
@@ -495,7 +496,7 @@ extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* v
 }
 
 // Copy-on-write copies and decode with append in one launch where the
-// GQA-4 kernel stores the new tokens; elsewhere pa_copy_blocks, then
+// partition kernel stores the new tokens; elsewhere pa_copy_blocks, then
 // pa_decode_append.
 extern "C" int pa_decode_append_cow(PA_DECODE_PARAMS, const void* key, const void* value,
                                     const int64_t* block_pairs, int num_pairs) {

@@ -131,25 +131,19 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0;
     const int id_lim = min(min(P / BS, 64), a.max_blocks_per_seq - lb0);
     int ids = lane < id_lim ? bt[lane] : 0;
-    const int T = a.seq_lens[seq];
+    const int T = load_uniform(a.seq_lens + seq);
     // copy-on-write pairs of this launch (decode with append only), one per
     // lane; -1 for lanes past them and for pairs outside the pool, which are
     // skipped as by pa_copy_blocks
     const bool cow = APPEND && a.cow_num > 0;
-    int cow_src = -1, cow_dst = -1;
-    if (cow && lane < a.cow_num) {
-        const int64_t s = a.cow_pairs[2 * lane];
-        const int64_t d = a.cow_pairs[2 * lane + 1];
-        const bool in_pool = s >= 0 && s < a.num_blocks && d >= 0 && d < a.num_blocks;
-        cow_src = in_pool ? (int)s : -1;
-        cow_dst = in_pool ? (int)d : -1;
-    }
+    CowPair pair{{0u, 0u, 0u, 0u}};
+    if constexpr (APPEND) pair = load_cow_pair(a, lane);
     // wait for the ids here, together with the length: the compiler does not
     // see the asynchronous copies below and would otherwise wait for them too
-    if constexpr (APPEND)
-        asm volatile("" : "+v"(ids), "+v"(cow_src), "+v"(cow_dst));
-    else
-        asm volatile("" : "+v"(ids));
+    asm volatile("" : "+v"(ids));
+    if constexpr (APPEND) pin_cow_pair(pair);
+    int cow_src = -1, cow_dst = -1;
+    if constexpr (APPEND) cow_pair_ids(a, pair, lane, cow_src, cow_dst);
     // A block that a pair of this launch overwrites is read from the pair's
     // source, which holds the same content once copied (the copying
     // workgroups run beside this one).  Each block id is checked when its
@@ -157,13 +151,7 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     // nothing stands between the ids' arrival and the first copies.  When
     // the sequence's last block is a destination, its copying workgroup
     // writes the new token into it, and this workgroup stores nothing there.
-    auto source_of = [&](int pb) {
-        if (cow) {
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(cow_dst == pb);
-            if (hit != 0) pb = __builtin_amdgcn_readlane(cow_src, (int)__builtin_ctzll(hit));
-        }
-        return pb;
-    };
+    auto source_of = [&](int pb) { return cow ? cow_source(cow_src, cow_dst, pb) : pb; };
     if (T <= 0 || T > a.max_seq_len) return;
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
     const int n_parts = (T + P - 1) / P;
@@ -429,80 +417,6 @@ __device__ __forceinline__ void gqa4_partition(const DecodeArgs& a, unsigned bid
     }
 }
 
-// Copy-on-write pair w / 2 of the launch, tensor w % 2 (K, then V): the
-// whole destination block (all kv heads, all rows) from the source block,
-// as pa_copy_blocks does.  When the destination is some sequence's last
-// block, the row of that sequence's new token is written from the new token
-// instead of from the source (the partition workgroups read the source for
-// that block and store nothing there).  These workgroups are the last of the
-// launch, so their chain of dependent memory accesses is kept short: the
-// owner search (each sequence's length, then its last block id) runs beside
-// the copy's loads, and no store waits for another.  NT threads.
-template <Fmt KV, int D, int BS, int NT>
-__device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    constexpr int ROW_G = D * FmtBytes<KV>::value / 16;  // 16-byte granules per row
-    constexpr int U = 8;                                 // granules per thread in flight
-    const int p = (int)(w >> 1);
-    const int z = (int)(w & 1);
-    const int s0 = (int)threadIdx.x;
-    // the first sequences' lengths, loaded with the pair
-    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
-    const int64_t src = a.cow_pairs[2 * p];
-    const int64_t dst = a.cow_pairs[2 * p + 1];
-    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;  // skipped pair
-    const int H = a.num_kv_heads;
-    const int granules = H * BS * ROW_G;  // one tensor's block: [kv head][row][granule]
-    u32x4* pool = (u32x4*)(z == 0 ? a.k_cache : a.v_cache);
-    const u32x4* from = pool + (size_t)src * granules;
-    u32x4* to = pool + (size_t)dst * granules;
-    const u32x4* tok = (const u32x4*)(z == 0 ? a.new_k : a.new_v);  // [seq][kv head][granule]
-    int* who = (int*)smem;  // the sequence whose last block is dst, and its new token's row
-    if (threadIdx.x == 0) who[0] = -1;
-
-    u32x4 v[U];
-    auto load = [&](int i0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (i0 + u * NT < granules) v[u] = from[i0 + u * NT];
-    };
-    auto store = [&](int i0, int s, int row) {
-        // the new token's granules are loaded together, then everything is stored
-        u32x4 t[U];
-        bool take[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * NT;
-            take[u] = s >= 0 && i < granules && (i / ROW_G) % BS == row;
-            if (take[u]) t[u] = tok[((size_t)s * H + i / (BS * ROW_G)) * ROW_G + i % ROW_G];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (i0 + u * NT < granules) to[i0 + u * NT] = take[u] ? t[u] : v[u];
-    };
-    auto owns = [&](int s, int T) {
-        return T > 0 && T <= a.max_seq_len && (T + BS - 1) / BS <= a.max_blocks_per_seq &&
-               a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / BS] == (int)dst;
-    };
-    load(s0);
-    const bool mine = s0 < a.num_seqs && owns(s0, T0);
-    __syncthreads();  // who[0] is initialised
-    // one sequence for valid input (destinations belong to one sequence)
-    if (mine) { who[0] = s0; who[1] = (T0 - 1) % BS; }
-    for (int s = s0 + NT; s < a.num_seqs; s += NT) {
-        const int T = a.seq_lens[s];
-        if (owns(s, T)) { who[0] = s; who[1] = (T - 1) % BS; }
-    }
-    __syncthreads();
-    const int s = who[0];
-    const int row = s >= 0 ? who[1] : -1;
-    store(s0, s, row);
-    for (int i0 = s0 + U * NT; i0 < granules; i0 += U * NT) {
-        load(i0);
-        store(i0, s, row);
-    }
-}
-
 template <Fmt KV, int D, int BS, int W, int S, bool APPEND>
 __global__ void __launch_bounds__(W * 64, (gqa_waves_per_simd<KV, D, BS, W, S>()))
 decode_partition_gqa4_kernel(const DecodeArgs a) {
@@ -529,7 +443,7 @@ int launch_partition_gqa4_as(const DecodeArgs& a, hipStream_t stream) {
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const size_t copies = APPEND ? 2 * (size_t)a.cow_num : 0;
+    const size_t copies = APPEND ? 2 * (size_t)a.cow_num * cow_chunks<KV, D, BS, W * 64>(a.num_kv_heads) : 0;
     const dim3 grid((unsigned)(copies + (size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

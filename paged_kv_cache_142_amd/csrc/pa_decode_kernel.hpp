@@ -231,8 +231,8 @@ __device__ __forceinline__ bool partition_work_item(const DecodeArgs& a, unsigne
     const int item = bid / a.num_kv_heads;
     kvh = bid - item * a.num_kv_heads;
     if (a.inline_plan) return inline_plan_item(a, item, seq, part);
-    if (item >= a.plan[0]) return false;
-    const int code = a.plan[PLAN_ITEMS_OFFSET + item];
+    if (item >= load_uniform(a.plan)) return false;
+    const int code = load_uniform(a.plan + PLAN_ITEMS_OFFSET + item);
     seq = code / a.max_partitions;
     part = code - seq * a.max_partitions;
     return true;
@@ -446,7 +446,131 @@ struct PartitionShape {
     static_assert(TILE % 1024 == 0, "a tile must be a whole number of 1 KiB wave copies");
     static_assert((S - 1) * DMA_PER_BLOCK <= 63, "vmcnt can count at most 63 copies");
     static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+    static_assert(ROWB % 16 == 0 && ROWB / 16 <= 64, "a row is copied as 16-byte granules, one per lane");
 };
+
+// Copy-on-write pairs in a decode launch: lane j < cow_num holds pair j
+// (source, destination).  load_cow_pair reads the lane's pair as given, as
+// four 32-bit words (the two little-endian int64 ids); cow_pair_ids checks it
+// once it has arrived, so that the caller can make the read resident together
+// with its other early reads (pin_cow_pair) instead of waiting for it on its
+// own.  Lanes past the pairs read the last one and are marked unused by the
+// check.  The read takes no branch (a branch would make the compiler wait for
+// it at once): a launch without pairs reads 16 bytes of the new keys instead,
+// which every decode-with-append launch has, and the check marks all lanes
+// unused.
+struct CowPair {
+    u32x4 w;
+};
+__device__ __forceinline__ CowPair load_cow_pair(const DecodeArgs& a, int lane) {
+    static_assert(COW_MAX_PAIRS <= 64, "one pair per lane");
+    const int64_t* p = a.cow_num > 0 ? a.cow_pairs + 2 * min(lane, a.cow_num - 1) : (const int64_t*)a.new_k;
+    const uint64_t s = (uint64_t)p[0], d = (uint64_t)p[1];
+    return {{(uint32_t)s, (uint32_t)(s >> 32), (uint32_t)d, (uint32_t)(d >> 32)}};
+}
+__device__ __forceinline__ void pin_cow_pair(CowPair& p) {
+    asm volatile("" : "+v"(p.w[0]), "+v"(p.w[1]), "+v"(p.w[2]), "+v"(p.w[3]));
+}
+// The pair's block ids; -1 for lanes past the pairs and for pairs outside
+// the pool, which are skipped as by pa_copy_blocks.
+__device__ __forceinline__ void cow_pair_ids(const DecodeArgs& a, const CowPair& p, int lane, int& cow_src,
+                                             int& cow_dst) {
+    const int64_t s = (int64_t)(((uint64_t)p.w[1] << 32) | p.w[0]);
+    const int64_t d = (int64_t)(((uint64_t)p.w[3] << 32) | p.w[2]);
+    const bool use = lane < a.cow_num && s >= 0 && s < a.num_blocks && d >= 0 && d < a.num_blocks;
+    cow_src = use ? (int)s : -1;
+    cow_dst = use ? (int)d : -1;
+}
+
+// The block a partition workgroup reads for physical block pb (wave-uniform):
+// the pair's source when pb is a destination of this launch (the same content
+// once copied; the copying workgroups run beside the partition ones), else
+// pb.  One compare of the pair lanes against pb and a ballot; every lane of
+// the wave must call it.
+__device__ __forceinline__ int cow_source(int cow_src, int cow_dst, int pb) {
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(cow_dst == pb);
+    if (hit != 0) pb = __builtin_amdgcn_readlane(cow_src, (int)__builtin_ctzll(hit));
+    return pb;
+}
+
+// Copy-on-write copies in a decode launch: each (pair, tensor) block copy is
+// split into chunks of COW_BATCH * NT 16-byte granules, one workgroup of NT
+// threads each, so that every copying workgroup needs one round of loads.
+constexpr int COW_BATCH = 8;  // granules per thread in flight
+template <Fmt KV, int D, int BS, int NT>
+__host__ __device__ inline int cow_chunks(int num_kv_heads) {
+    const int granules = num_kv_heads * BS * (D * FmtBytes<KV>::value / 16);
+    return (granules + COW_BATCH * NT - 1) / (COW_BATCH * NT);
+}
+
+// Copying workgroup w of the launch: chunk w % C of pair w / C / 2, tensor
+// w / C % 2 (K, then V), C = cow_chunks: that part of the destination block
+// (all kv heads, all rows) from the source block, as pa_copy_blocks does.
+// When the destination is some sequence's last block, the row of that
+// sequence's new token is written from the new token instead of from the
+// source (the partition workgroups read the source for that block and store
+// nothing there).  These workgroups are the last of the launch, so their
+// chain of dependent memory accesses is kept short: the owner search (each
+// sequence's length, then its last block id) runs beside the copy's loads,
+// and no store waits for another.
+template <Fmt KV, int D, int BS, int NT>
+__device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    constexpr int ROW_G = D * FmtBytes<KV>::value / 16;  // 16-byte granules per row
+    constexpr int U = COW_BATCH;
+    const int H = a.num_kv_heads;
+    const int chunks = cow_chunks<KV, D, BS, NT>(H);
+    const int pt = (int)(w / (unsigned)chunks);
+    const int chunk = (int)w - pt * chunks;
+    const int p = pt >> 1;
+    const int z = pt & 1;
+    const int s0 = (int)threadIdx.x;
+    // the first sequences' lengths, loaded with the pair
+    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
+    const int64_t src = a.cow_pairs[2 * p];
+    const int64_t dst = a.cow_pairs[2 * p + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;  // skipped pair
+    const int granules = H * BS * ROW_G;  // one tensor's block: [kv head][row][granule]
+    u32x4* pool = (u32x4*)(z == 0 ? a.k_cache : a.v_cache);
+    const u32x4* from = pool + (size_t)src * granules;
+    u32x4* to = pool + (size_t)dst * granules;
+    const u32x4* tok = (const u32x4*)(z == 0 ? a.new_k : a.new_v);  // [seq][kv head][granule]
+    int* who = (int*)smem;  // the sequence whose last block is dst, and its new token's row
+    if (threadIdx.x == 0) who[0] = -1;
+
+    const int i0 = chunk * U * NT + s0;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < granules) v[u] = from[i0 + u * NT];
+    auto owns = [&](int s, int T) {
+        return T > 0 && T <= a.max_seq_len && (T + BS - 1) / BS <= a.max_blocks_per_seq &&
+               a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / BS] == (int)dst;
+    };
+    const bool mine = s0 < a.num_seqs && owns(s0, T0);
+    __syncthreads();  // who[0] is initialised
+    // one sequence for valid input (destinations belong to one sequence)
+    if (mine) { who[0] = s0; who[1] = (T0 - 1) % BS; }
+    for (int s = s0 + NT; s < a.num_seqs; s += NT) {
+        const int T = a.seq_lens[s];
+        if (owns(s, T)) { who[0] = s; who[1] = (T - 1) % BS; }
+    }
+    __syncthreads();
+    const int s = who[0];
+    const int row = s >= 0 ? who[1] : -1;
+    // the new token's granules are loaded together, then everything is stored
+    u32x4 t[U];
+    bool take[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        take[u] = s >= 0 && i < granules && (i / ROW_G) % BS == row;
+        if (take[u]) t[u] = tok[((size_t)s * H + i / (BS * ROW_G)) * ROW_G + i % ROW_G];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < granules) to[i0 + u * NT] = take[u] ? t[u] : v[u];
+}
 
 // Wait until at most n whole blocks (0 <= n <= N) of copies are in flight.
 template <int PER_BLOCK, int N>
@@ -462,9 +586,10 @@ __device__ __forceinline__ void wait_blocks_in_flight(int n) {
     }
 }
 
-template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S>
-__global__ void __launch_bounds__(W * 64)
-decode_partition_kernel(const DecodeArgs a) {
+// The partition workgroup's work (generic kernel).  APPEND: decode with
+// append, with the launch's copy-on-write pairs (the kernel below).
+template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S, bool APPEND>
+__device__ __forceinline__ void generic_partition(const DecodeArgs& a, unsigned bid) {
     using Sh = PartitionShape<KV, D, BS, G, W, S>;
     using Row = LaneRow<KV, D>;
     using Dot = QK<KV, Q>;
@@ -477,9 +602,13 @@ decode_partition_kernel(const DecodeArgs a) {
     const int r = lane / LPR;
     const int c = lane % LPR;
     int seq, kvh, part;
-    if (!partition_work_item(a, seq, kvh, part)) return;
+    if (!partition_work_item(a, bid, seq, kvh, part)) return;
 
-    const int T = a.seq_lens[seq];
+    const int T = load_uniform(a.seq_lens + seq);
+    // copy-on-write pairs of this launch (decode with append only)
+    const bool cow = APPEND && a.cow_num > 0;
+    CowPair pair{{0u, 0u, 0u, 0u}};
+    if constexpr (APPEND) pair = load_cow_pair(a, lane);
     if (T <= 0 || T > a.max_seq_len) return;  // empty or invalid rows: written by the reduce kernel
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
     const int P = a.partition_size;
@@ -499,6 +628,23 @@ decode_partition_kernel(const DecodeArgs a) {
     int ids = lane < nbw ? bt[lane] : 0;
     const int hq0 = kvh * G;
 
+    // Decode with append: the wave that stages the sequence's last block
+    // holds the newest token's K and V rows of this kv head in registers (one
+    // 16-byte granule of each per lane), writes them over that row of the
+    // staged block once the block has landed, and stores them into the pool;
+    // the attention never depends on when the store reaches memory.  Kept in
+    // registers rather than LDS, so that the appending kernel's LDS footprint
+    // (and with it the workgroups resident per CU) is the plain kernel's.
+    const bool appends = APPEND && part == n_parts - 1 && nbw > 0 && kb0 + nbw == nblk;
+    const int new_row = (T - 1) % BS;  // row of the newest token in its block
+    constexpr int NEWG = ROWB / 16;    // 16-byte granules of a row
+    u32x4 new_kg = {0u, 0u, 0u, 0u}, new_vg = {0u, 0u, 0u, 0u};
+    if (appends && lane < NEWG) {
+        const size_t src = ((size_t)seq * a.num_kv_heads + kvh) * ROWB + lane * 16;
+        new_kg = *(const u32x4*)((const char*)a.new_k + src);
+        new_vg = *(const u32x4*)((const char*)a.new_v + src);
+    }
+
     // Query operands of the G heads (the lane's 8 elements of each).
     typename Dot::Op qop[G];
     {
@@ -509,7 +655,14 @@ decode_partition_kernel(const DecodeArgs a) {
         // the compiler's own wait for them cannot also wait for the copies
 #pragma unroll
         for (int g = 0; g < G; ++g) qop[g].pin();
+        if constexpr (APPEND) {  // the pairs and the new rows too, loaded first
+            pin_cow_pair(pair);
+            asm volatile("" : "+v"(new_kg[0]), "+v"(new_kg[1]), "+v"(new_kg[2]), "+v"(new_kg[3]));
+            asm volatile("" : "+v"(new_vg[0]), "+v"(new_vg[1]), "+v"(new_vg[2]), "+v"(new_vg[3]));
+        }
     }
+    int cow_src = -1, cow_dst = -1;
+    if constexpr (APPEND) cow_pair_ids(a, pair, lane, cow_src, cow_dst);
     float qk_scale = a.qk_scale_log2;
     // The value scale is needed only by the final stores, but a load issued
     // there would add a memory round trip to every workgroup's end; both
@@ -517,8 +670,8 @@ decode_partition_kernel(const DecodeArgs a) {
     // queries.
     float vs = 1.f;
     if constexpr (KV == Fmt::FP8) {
-        float ks = a.k_scale[kvh];
-        vs = a.v_scale[kvh];
+        float ks = load_uniform(a.k_scale + kvh);
+        vs = load_uniform(a.v_scale + kvh);
         asm volatile("" : "+v"(ks), "+v"(vs));
         qk_scale *= ks;
     }
@@ -538,6 +691,7 @@ decode_partition_kernel(const DecodeArgs a) {
         }
         int pb = __builtin_amdgcn_readlane(ids, k & 63);
         if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
+        if (cow) pb = cow_source(cow_src, cow_dst, pb);
         const size_t tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)lane * 16;
         const uint32_t dst = ring_lds + (uint32_t)(stage * Sh::STAGE);
 #pragma unroll
@@ -619,6 +773,23 @@ decode_partition_kernel(const DecodeArgs a) {
     for (int k = 0; k < nbw; ++k) {
         if (k + S - 1 < nbw) issue(k + S - 1, stage == 0 ? S - 1 : stage - 1);
         wait_blocks_in_flight<Sh::DMA_PER_BLOCK, S - 1>(min(S - 1, nbw - 1 - k));
+        if (appends && k == nbw - 1) {
+            // the block's own id (the ids window holding it is the current one)
+            const int pb = __builtin_amdgcn_readlane(ids, k & 63);
+            // a copy-on-write destination gets the token from its copying workgroup
+            const bool stores = !cow || cow_source(cow_src, cow_dst, pb) == pb;
+            if (lane < NEWG) {
+                const u32x4 kg = new_kg, vg = new_vg;
+                char* row = ring + stage * Sh::STAGE + new_row * ROWB + lane * 16;
+                *(u32x4*)row = kg;
+                *(u32x4*)(row + TILE) = vg;
+                if (stores && (unsigned)pb < (unsigned)a.num_blocks) {
+                    const size_t dst = ((size_t)pb * a.num_kv_heads + kvh) * TILE + (size_t)new_row * ROWB + lane * 16;
+                    *(u32x4*)((char*)a.k_cache + dst) = kg;
+                    *(u32x4*)((char*)a.v_cache + dst) = vg;
+                }
+            }
+        }
         const char* kb = ring + stage * Sh::STAGE;
         const int blk_tok0 = (lb0 + kb0 + k) * BS;
         if (blk_tok0 + BS <= T) {
@@ -736,17 +907,44 @@ decode_partition_kernel(const DecodeArgs a) {
     }
 }
 
+template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S, bool APPEND>
+__global__ void __launch_bounds__(W * 64)
+decode_partition_kernel(const DecodeArgs a) {
+    if constexpr (APPEND) {
+        // decode with append: the copy-on-write pairs' workgroups come last,
+        // where the tail of the partition work leaves slots idle (nothing here
+        // reads their destinations)
+        const unsigned parts = (unsigned)a.num_seqs * (unsigned)a.max_partitions * (unsigned)a.num_kv_heads;
+        if (blockIdx.x >= parts) {
+            cow_copy_block<KV, D, BS, W * 64>(a, blockIdx.x - parts);
+            return;
+        }
+    }
+    generic_partition<KV, Q, D, BS, G, W, S, APPEND>(a, blockIdx.x);
+}
+
 // Launch one partition-kernel instantiation (sets the LDS attribute once).
+template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S, bool APPEND>
+int launch_partition_as(const DecodeArgs& a, hipStream_t stream) {
+    using Sh = PartitionShape<KV, D, BS, G, W, S>;
+    constexpr int LDS = Sh::LDS;
+    auto kernel = decode_partition_kernel<KV, Q, D, BS, G, W, S, APPEND>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess) return PA_ERR_LAUNCH;
+    const size_t copies = APPEND ? 2 * (size_t)a.cow_num * cow_chunks<KV, D, BS, W * 64>(a.num_kv_heads) : 0;
+    const dim3 grid((unsigned)(copies + (size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
+    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), LDS, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// The plain kernel, or the one that also stores the new tokens and makes the
+// launch's copy-on-write copies (decode with append): separate
+// instantiations, so that the plain one carries none of it.
 template <Fmt KV, Fmt Q, int D, int BS, int G, int W, int S>
 int launch_partition(const DecodeArgs& a, hipStream_t stream) {
-    using Sh = PartitionShape<KV, D, BS, G, W, S>;
-    auto kernel = decode_partition_kernel<KV, Q, D, BS, G, W, S>;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
-    if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
-    hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    return a.new_k != nullptr ? launch_partition_as<KV, Q, D, BS, G, W, S, true>(a, stream)
+                              : launch_partition_as<KV, Q, D, BS, G, W, S, false>(a, stream);
 }
 
 // Shared-prefix partition states (pa_decode_prefix.hip): whether the

@@ -1,12 +1,15 @@
 """pa_decode_append_cow on the GPU: the copy-on-write copies, the new tokens'
 store and the decode in one call give bitwise the pools and outputs of
 pa_copy_blocks followed by pa_decode_append -- with destinations no table
-names (the decode reads none of them), with a pair outside the pool (skipped
-by both), and in a fork: two sequences share their last block, one of them
+names (the decode reads none of them; their sources are blocks no sequence
+appends to this step, as the call requires), with a pair outside the pool
+(skipped by both), and in a fork: two sequences share their last block, one of them
 has been given a private copy that this step makes, and both append their new
 token at the same row.  The fork's output is also checked against the oracle
-(copy, then store, then decode, from pools it builds itself).  Shapes outside
-the one-launch path (G = 1) make the two calls and must agree as well.
+(copy, then store, then decode, from pools it builds itself).  The GQA-4
+kernel and the generic kernel (every other group and format) take the copies
+in their launch; the FP8 matrix-core shape (G = 8, head_dim 128) and more
+than 16 pairs make the two calls and must agree as well.
 
 The copy-on-write steps follow the explainer's section "Copy-on-Write（CoW）に
 よるメモリ共有" (copy the shared block, remap the writer's table entry)."""
@@ -43,6 +46,20 @@ def _new_tokens(case, wl):
     return full_k, full_v
 
 
+def _sources_off_last_blocks(wl, seed):
+    """The workload's pairs with every source moved off the blocks the step
+    appends to (sequences' last blocks): a pair from such a block to a
+    destination no appending sequence owns would race with the store of the
+    new token (pagedattn.h, pa_decode_append_cow)."""
+    B = wl.block_size
+    lens = wl.seq_lens.astype(np.int64)
+    last = {int(wl.block_tables[i, (t - 1) // B]) for i, t in enumerate(lens) if t > 0}
+    named = wl.block_tables[wl.block_tables >= 0].ravel()
+    pool = np.array(sorted({int(b) for b in named} - last), np.int64)
+    src = np.random.default_rng(seed).choice(pool, size=len(wl.copy_pairs), replace=False)
+    return np.stack([src, wl.copy_pairs[:, 1]], axis=1).astype(np.int64)
+
+
 def _run(wl, pairs_np):
     """(output, K pool, V pool) bytes of the one call and of the two calls."""
     res = []
@@ -76,18 +93,37 @@ def test_cow_spare_destinations_match_two_calls(kv, block, P, npairs):
         f"cow_spare_{kv}_{block}_{P}", 7, seq_lens=np.random.default_rng(7).integers(1, 3000, size=24),
         num_heads=32, num_kv_heads=8, head_dim=128, block_size=block, kv_dtype=kv, q_dtype=kv, spare_blocks=48,
         num_copy_pairs=npairs, partition_size=P)
-    pairs = np.concatenate([wl.copy_pairs, [[wl.num_blocks + 5, int(wl.copy_pairs[0, 1])]]])  # one pair outside the pool
+    spare = _sources_off_last_blocks(wl, 71)
+    pairs = np.concatenate([spare, [[wl.num_blocks + 5, int(spare[0, 1])]]])  # one pair outside the pool
     print(f"[case] cow spare {wl.name}: {len(pairs)} pairs", flush=True)
     _run(wl, pairs)
 
 
-def _fork_workload(kv, block, lens, P):
+@pytest.mark.parametrize("kv,q,heads,kv_heads,dim,block,P,npairs", [
+    ("f16", "f16", 40, 40, 128, 16, 512, 15),     # G = 1, 40 kv heads: each block copy in 10 chunks
+    ("f32", "f32", 8, 4, 64, 16, 256, 15),        # G = 2, fp32
+    ("fp8_e4m3", "bf16", 32, 8, 128, 16, 512, 12),  # FP8 through the generic kernel (G = 4)
+    ("bf16", "bf16", 64, 8, 128, 32, 512, 15),    # G = 8, 16-bit
+    ("fp8_e4m3", "bf16", 64, 8, 128, 16, 512, 10),  # FP8 matrix-core shape: the two calls
+])
+def test_cow_generic_shapes_match_two_calls(kv, q, heads, kv_heads, dim, block, P, npairs):
+    wl = workloads.build_decode_workload(
+        f"cow_gen_{kv}_{heads}_{kv_heads}_{dim}_{block}", 9, seq_lens=np.random.default_rng(9).integers(1, 1500, size=20),
+        num_heads=heads, num_kv_heads=kv_heads, head_dim=dim, block_size=block, kv_dtype=kv, q_dtype=q,
+        spare_blocks=40, num_copy_pairs=npairs, partition_size=P)
+    spare = _sources_off_last_blocks(wl, 91)
+    pairs = np.concatenate([spare, [[-3, int(spare[0, 1])]]])  # one pair outside the pool
+    print(f"[case] cow generic {wl.name}: {len(pairs)} pairs", flush=True)
+    _run(wl, pairs)
+
+
+def _fork_workload(kv, block, lens, P, heads=32, kv_heads=8):
     """Sequences 0 and 1 share every block (the same length); sequence 0's
     last block has been given a private copy (a block no table named), and
     sequence 2's first block too; the pairs make those copies."""
     wl = workloads.build_decode_workload(
-        f"cow_fork_{kv}_{block}_{P}", 11, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
-        block_size=block, kv_dtype=kv, q_dtype=kv, spare_blocks=8, num_copy_pairs=0, partition_size=P)
+        f"cow_fork_{kv}_{block}_{P}_{heads}_{kv_heads}", 11, seq_lens=lens, num_heads=heads, num_kv_heads=kv_heads,
+        head_dim=128, block_size=block, kv_dtype=kv, q_dtype=kv, spare_blocks=8, num_copy_pairs=0, partition_size=P)
     bt = wl.block_tables.copy()
     assert lens[0] == lens[1]
     bt[1] = bt[0]  # sequence 1 now shares sequence 0's blocks (its own become unreferenced)
@@ -116,13 +152,15 @@ def _oracle_after(wl, pairs, key_raw, value_raw):
     return kc, vc, out
 
 
-@pytest.mark.parametrize("kv,block,lens", [
-    ("bf16", 16, [65, 65, 300, 40, 1000]),    # new token at the first row of a block
-    ("bf16", 16, [80, 80, 17, 2000, 5]),      # at the last row
-    ("f16", 32, [33, 33, 640, 1, 129]),
+@pytest.mark.parametrize("kv,block,lens,heads,kv_heads", [
+    ("bf16", 16, [65, 65, 300, 40, 1000], 32, 8),    # new token at the first row of a block
+    ("bf16", 16, [80, 80, 17, 2000, 5], 32, 8),      # at the last row
+    ("f16", 32, [33, 33, 640, 1, 129], 32, 8),
+    ("f16", 16, [80, 80, 17, 2000, 5], 16, 16),      # the generic kernel (G = 1)
+    ("bf16", 32, [65, 65, 300, 40, 1000], 16, 8),    # the generic kernel (G = 2)
 ])
-def test_cow_fork_matches_two_calls_and_oracle(kv, block, lens):
-    wl, pairs = _fork_workload(kv, block, np.array(lens), 512)
+def test_cow_fork_matches_two_calls_and_oracle(kv, block, lens, heads, kv_heads):
+    wl, pairs = _fork_workload(kv, block, np.array(lens), 512, heads, kv_heads)
     print(f"[case] cow fork {wl.name}: lens {lens}, pairs {pairs.tolist()}", flush=True)
     case = _run(wl, pairs)
     st = wl.step_rows()
@@ -137,7 +175,7 @@ def test_cow_fork_matches_two_calls_and_oracle(kv, block, lens):
     assert_close(out_as_f64(case.out), want, TOL[kv], "fork decode vs oracle")
 
 
-def test_cow_other_shapes_make_the_two_calls():
+def test_cow_g1_matches_two_calls():
     wl = workloads.build_decode_workload(
         "cow_g1", 3, seq_lens=[5, 300, 17, 1024], num_heads=8, num_kv_heads=8, head_dim=128, block_size=16,
         kv_dtype="f16", q_dtype="f16", spare_blocks=8, num_copy_pairs=4, partition_size=512)

@@ -3,14 +3,15 @@
 A step is one pass of the whole path over the batch: the step's block
 copies (``pa_copy_blocks``), the scatter of each sequence's new token into
 the pool, and the decode itself.  Where one call can do the last two
-(bf16/f16/f32 pools), the step is one ``pa_decode_append_cow`` call: for
-four query heads per kv head its partition launch also makes the copies
-and stores the tokens, elsewhere it is ``pa_copy_blocks`` then
-``pa_decode_append`` (``--separate-cow``: those two calls everywhere).  The
+(bf16/f16/f32 pools), the step is one ``pa_decode_append_cow`` call: its
+partition launch also makes the copies and stores the tokens
+(``--separate-cow``: ``pa_copy_blocks`` then ``pa_decode_append``).  The
 grouped shared-prefix workloads run ``pa_copy_blocks`` then
 ``pa_decode_shared_prefix`` given the new tokens.  For FP8 pools (quantized
-on write) it is the scatter (``pa_reshape_and_cache_fp8``), the copies, and
-the decode (``pa_decode_partition`` then ``pa_decode_reduce``).
+on write) it is the scatter (``pa_reshape_and_cache_fp8``), then
+``pa_decode_append_cow`` without tokens: the copies in the matrix-core
+partition launch, then the reduce (``--separate-cow``: ``pa_copy_blocks``,
+``pa_decode_partition``, ``pa_decode_reduce``).
 ``step_calls`` in the output names them.
 Inputs are resident in HBM before the timed region.  Throughput is the
 effective KV bandwidth: sum_i T_i * 2 * H_kv * d * b_kv bytes per step.
@@ -402,7 +403,7 @@ class Device:
         # as a launch of their own before it
         self.separate_cow = separate_cow
         # identical calls every step: marshal the C arguments once per pool copy
-        self.call_sets = [self._make_calls(kc, vc, fused=self.append_fused) for kc, vc in self.pools]
+        self.call_sets = [self._step_calls(kc, vc) for kc, vc in self.pools]
         self.part_sets = [self._make_calls(kc, vc) for kc, vc in self.pools]
         self.decode_calls = [self._decode_call(kc, vc) for kc, vc in self.pools]
         # decode with append alone (no copies), for the per-call times
@@ -417,6 +418,17 @@ class Device:
         if self.groups is not None:
             return self.pa.prepared("pa_decode_shared_prefix", **dargs, **self.groups)
         return self.pa.prepared("pa_decode", **dargs)
+
+    def _step_calls(self, k_cache=None, v_cache=None):
+        """The timed step's calls.  FP8 pools: the quantize-on-write scatter,
+        then the copies and the decode in one call given no tokens."""
+        if self.quantize_step and not self.separate_cow and self.groups is None and self.pairs.numel():
+            calls = self._make_calls(k_cache, v_cache)
+            kc = self.k_cache if k_cache is None else k_cache
+            vc = self.v_cache if v_cache is None else v_cache
+            return [calls[0], self.pa.prepared("pa_decode_append_cow", **dict(self.dargs, k_cache=kc, v_cache=vc),
+                                               key=None, value=None, block_pairs=self.pairs)]
+        return self._make_calls(k_cache, v_cache, fused=self.append_fused)
 
     def _make_calls(self, k_cache=None, v_cache=None, fused=False):
         pa, kv = self.pa, self.kv
@@ -457,7 +469,7 @@ class Device:
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                calls = self._make_calls(fused=self.append_fused)
+                calls = self._step_calls()
                 for call in calls:
                     call()
         torch.cuda.current_stream().wait_stream(side)
@@ -756,6 +768,8 @@ def main():
         k_us["decode_partition"] = back_to_back(torch, [c[2] for c in dev.part_sets], n)
         k_us["decode_reduce"] = back_to_back(torch, [c[3] for c in dev.part_sets], n)
     k_us["decode"] = decode_alone_us
+    if dev.quantize_step and len(dev.call_sets[0]) == 2:  # the copies and the decode in one call
+        k_us["decode_cow"] = back_to_back(torch, [c[1] for c in dev.call_sets], n)
     if dev.append_calls:
         k_us["decode_append"] = back_to_back(torch, dev.append_calls, n)
         if not dev.separate_cow:
@@ -804,6 +818,8 @@ def main():
                         else ["pa_copy_blocks", "pa_decode_append"] if dev.separate_cow
                         else ["pa_decode_append_cow (the copies and the new tokens' store in the decode launch, "
                               "but for the FP8 matrix-core shape: there pa_copy_blocks, then pa_decode_append)"]) if dev.append_fused else
+                       ["pa_reshape_and_cache_fp8", "pa_decode_append_cow (no tokens: the copies in the "
+                        "matrix-core partition launch, then the reduce)"] if len(dev.call_sets[0]) == 2 else
                        ["pa_reshape_and_cache" + ("_fp8" if dev.quantize_step else ""), "pa_copy_blocks",
                         "pa_decode_shared_prefix" if groups is not None else "pa_decode_partition",
                         *([] if groups is not None else ["pa_decode_reduce"])]),

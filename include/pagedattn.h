@@ -370,9 +370,15 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
  * sequence's last block its copying workgroups write that sequence's new
  * token in place of the copied row.  Other shapes and more pairs make the
  * two calls.
+ * key and value may both be null: the call is then pa_copy_blocks followed
+ * by pa_decode (no token is stored; a step that stores its tokens another
+ * way, such as pa_reshape_and_cache_fp8, makes that call first).  For the
+ * FP8 matrix-core shape this runs as one launch as well, the copies and
+ * the per-block source check as above; other shapes make the two calls.
  *   block_pairs  int64 [num_pairs][2] (source, destination), device; pairs
  *                outside the pool are skipped, as by pa_copy_blocks
- *   num_pairs    >= 0; 0 makes this pa_decode_append
+ *   num_pairs    >= 0; 0 makes this pa_decode_append (pa_decode without
+ *                new rows)
  *   other arguments: as for pa_decode_append.  Preconditions of
  *                pa_copy_blocks: destinations are distinct and none is a
  *                source; a destination belongs to at most one sequence.
@@ -385,7 +391,8 @@ int pa_decode_append(void* out, int out_dtype, const void* q, int q_dtype, const
  *                token, and only then does the copy hold the right one (the
  *                appending sequence's own).
  * Errors: PA_ERR_SHAPE for num_pairs < 0, PA_ERR_NULL for a null block_pairs
- * with num_pairs > 0, otherwise those of the two calls.
+ * with num_pairs > 0 or for exactly one of key and value null (before any
+ * launch), otherwise those of the two calls.
  */
 int pa_decode_append_cow(void* out, int out_dtype, const void* q, int q_dtype, const void* k_cache,
                          const void* v_cache, int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,

@@ -158,7 +158,7 @@ def prepared(name, *args, **kw):
         argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw)
     elif name == "pa_decode_append_cow":
         key, value, pairs = kw.pop("key"), kw.pop("value"), kw.pop("block_pairs")
-        argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw) + _pairs_argv(pairs)
+        argv = _decode_argv(*args, **kw) + _append_argv_opt(key, value, args, kw) + _pairs_argv(pairs)
     elif name == "pa_decode_shared_prefix":
         gs, gp, mgs, mpl = (kw.pop(k) for k in ("group_start", "group_prefix", "max_group_size", "max_prefix_len"))
         key, value = kw.pop("key", None), kw.pop("value", None)
@@ -228,6 +228,15 @@ def _append_argv(key, value, args, kw):
     return (_ptr(key), _ptr(value))
 
 
+def _append_argv_opt(key, value, args, kw):
+    """The new rows, or two null pointers when neither is given."""
+    if key is None and value is None:
+        return (None, None)
+    if key is None or value is None:
+        raise ValueError("give both key and value, or neither")
+    return _append_argv(key, value, args, kw)
+
+
 def pa_decode_append(*args, key, value, **kw):
     """``pa_decode`` that first stores each sequence's newest token
     (``key``/``value`` ``[num_seqs][num_kv_heads][head_dim]``) at position
@@ -239,8 +248,9 @@ def pa_decode_append(*args, key, value, **kw):
 def pa_decode_append_cow(*args, key, value, block_pairs, **kw):
     """``pa_copy_blocks`` with ``block_pairs`` (int64 ``[P][2]`` (source,
     destination), device), then ``pa_decode_append``; one launch where the
-    GQA-4 kernel stores the new tokens."""
-    argv = _decode_argv(*args, **kw) + _append_argv(key, value, args, kw) + _pairs_argv(block_pairs)
+    partition kernel stores the new tokens.  ``key=None, value=None``: the
+    copies, then ``pa_decode`` (one launch for the FP8 matrix-core shape)."""
+    argv = _decode_argv(*args, **kw) + _append_argv_opt(key, value, args, kw) + _pairs_argv(block_pairs)
     _check(_lib.load().pa_decode_append_cow(*argv), "pa_decode_append_cow")
 
 

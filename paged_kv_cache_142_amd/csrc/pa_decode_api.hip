@@ -386,13 +386,22 @@ __global__ void __launch_bounds__(256) append_tokens_kernel(const u32x4* __restr
 // launch's copy-on-write pairs): the GQA-4 kernel when a partition has at
 // most 64 blocks (their ids sit in one vector register), and the generic
 // kernel.  The FP8 matrix-core kernel does not.
+static bool partition_kernel_is_mfma8(const Prepared& pr);
 static bool partition_appends(const Prepared& pr) {
     if (partition_kernel_is_gqa4(pr.kv_dtype, pr.group))
         return pr.args.partition_size / pr.args.block_size <= 64;
+    return !partition_kernel_is_mfma8(pr);
+}
+
+// The FP8 matrix-core kernel (it takes copy-on-write pairs, but stores no
+// new tokens).
+static bool partition_kernel_is_mfma8(const Prepared& pr) {
 #ifndef PA_DISABLE_MFMA8
-    if (pr.kv_dtype == PA_DTYPE_FP8_E4M3 && pr.group == 8 && pr.head_dim == 128) return false;
+    return pr.kv_dtype == PA_DTYPE_FP8_E4M3 && pr.group == 8 && pr.head_dim == 128;
+#else
+    (void)pr;
+    return false;
 #endif
-    return true;
 }
 
 static int run_reduce(const Prepared& pr, hipStream_t stream) {
@@ -497,25 +506,30 @@ extern "C" int pa_decode_append(PA_DECODE_PARAMS, const void* key, const void* v
 
 // Copy-on-write copies and decode with append in one launch where the
 // partition kernel stores the new tokens; elsewhere pa_copy_blocks, then
-// pa_decode_append.
+// pa_decode_append.  With no new tokens (key and value both null): the
+// copies and the decode, in one launch for the FP8 matrix-core shape, else
+// pa_copy_blocks, then pa_decode.
 extern "C" int pa_decode_append_cow(PA_DECODE_PARAMS, const void* key, const void* value,
                                     const int64_t* block_pairs, int num_pairs) {
     if (num_pairs < 0) return PA_ERR_SHAPE;
     if (num_pairs > 0 && !block_pairs) return PA_ERR_NULL;
+    const bool tokens = key != nullptr || value != nullptr;
     pa::Prepared pr;
     const int st = pa::prepare(pr, PA_DECODE_ARGS);
     if (st != PA_OK) return st;
     const bool fused = num_pairs > 0 && !pr.nothing_to_do && pr.args.max_partitions > 0 &&
-                       num_pairs <= pa::COW_MAX_PAIRS && pa::partition_appends(pr) &&
+                       num_pairs <= pa::COW_MAX_PAIRS &&
+                       (tokens ? pa::partition_appends(pr) : pa::partition_kernel_is_mfma8(pr)) &&
                        (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
     if (!fused) {
+        if (tokens && (!key || !value)) return PA_ERR_NULL;
         const int c = pa_copy_blocks((void*)k_cache, (void*)v_cache, block_pairs, num_pairs, num_kv_heads,
                                      head_dim, block_size, num_blocks, kv_dtype, stream);
         if (c != PA_OK) return c;
-        return pa_decode_append(PA_DECODE_ARGS, stream, key, value);
+        return tokens ? pa_decode_append(PA_DECODE_ARGS, stream, key, value) : pa_decode(PA_DECODE_ARGS, stream);
     }
-    if (!key || !value) return PA_ERR_NULL;
-    if (!pa::aligned16(key) || !pa::aligned16(value)) return PA_ERR_SHAPE;
+    if (tokens && (!key || !value)) return PA_ERR_NULL;
+    if (tokens && (!pa::aligned16(key) || !pa::aligned16(value))) return PA_ERR_SHAPE;
     PA_CHECK_SEQUENCES();
 #if PA_CHECK_CONTENTS
     const int cp = pa::check::pairs(block_pairs, num_pairs, num_blocks, num_blocks, true, (hipStream_t)stream);

@@ -525,8 +525,11 @@ __device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
     const int p = pt >> 1;
     const int z = pt & 1;
     const int s0 = (int)threadIdx.x;
+    // a launch given no new tokens (copies and decode only) writes no row
+    // from them: the owner search is skipped
+    const bool tokens = a.new_k != nullptr;
     // the first sequences' lengths, loaded with the pair
-    const int T0 = s0 < a.num_seqs ? a.seq_lens[s0] : 0;
+    const int T0 = tokens && s0 < a.num_seqs ? a.seq_lens[s0] : 0;
     const int64_t src = a.cow_pairs[2 * p];
     const int64_t dst = a.cow_pairs[2 * p + 1];
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;  // skipped pair
@@ -547,11 +550,11 @@ __device__ void cow_copy_block(const DecodeArgs& a, unsigned w) {
         return T > 0 && T <= a.max_seq_len && (T + BS - 1) / BS <= a.max_blocks_per_seq &&
                a.block_tables[(size_t)s * a.max_blocks_per_seq + (T - 1) / BS] == (int)dst;
     };
-    const bool mine = s0 < a.num_seqs && owns(s0, T0);
+    const bool mine = tokens && s0 < a.num_seqs && owns(s0, T0);
     __syncthreads();  // who[0] is initialised
     // one sequence for valid input (destinations belong to one sequence)
     if (mine) { who[0] = s0; who[1] = (T0 - 1) % BS; }
-    for (int s = s0 + NT; s < a.num_seqs; s += NT) {
+    for (int s = s0 + NT; tokens && s < a.num_seqs; s += NT) {
         const int T = a.seq_lens[s];
         if (owns(s, T)) { who[0] = s; who[1] = (T - 1) % BS; }
     }

@@ -119,12 +119,24 @@ __device__ __forceinline__ float max_over_groups(float x) {
 #define PA_MFMA_WAVES_PER_SIMD 2
 #endif
 
-template <int D, int BS, int W, int S>
+// COW: the launch also makes its copy-on-write copies (up to COW_MAX_PAIRS
+// pairs, no new tokens): the copying workgroups come last in the grid, and a
+// partition workgroup reads a destination block from its pair's source,
+// checked per block when its copies are issued.
+template <int D, int BS, int W, int S, bool COW>
 __global__ void __launch_bounds__(W * 64, PA_MFMA_WAVES_PER_SIMD)
 decode_partition_mfma8_kernel(const DecodeArgs a) {
     using Sh = MfmaShape<D, BS, W, S>;
     constexpr int G = Sh::G, ROWB = Sh::ROWB, TILE = Sh::TILE, BPU = Sh::BPU, NA = Sh::NA;
     extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    if constexpr (COW) {
+        const unsigned parts = (unsigned)a.num_seqs * (unsigned)a.max_partitions * (unsigned)a.num_kv_heads;
+        if (blockIdx.x >= parts) {
+            cow_copy_block<Fmt::FP8, D, BS, W * 64>(a, blockIdx.x - parts);
+            return;
+        }
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -141,11 +153,13 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     const int32_t* bt = a.block_tables + (size_t)seq * a.max_blocks_per_seq + lb0;
     const int id_lim = min(min(P / BS, 64), a.max_blocks_per_seq - lb0);
     int ids = lane < id_lim ? bt[lane] : 0;
-    const int T = a.seq_lens[seq];
-    float k_scale = a.k_scale[kvh];
+    const int T = load_uniform(a.seq_lens + seq);
+    float k_scale = load_uniform(a.k_scale + kvh);
     // the value scale is used only by the final stores; loaded here, with the
     // ids, it adds no memory round trip to the workgroup's end
-    float vs = a.v_scale[kvh];
+    float vs = load_uniform(a.v_scale + kvh);
+    CowPair pair{{0u, 0u, 0u, 0u}};
+    if constexpr (COW) pair = load_cow_pair(a, lane);
     // Query operand: head n's elements 32 g .. 32 g + 31 (zero for n >= G).
     bf16x8 qop[Sh::NC];
     {
@@ -163,6 +177,11 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     asm volatile("" : "+v"(ids), "+v"(k_scale), "+v"(vs));
 #pragma unroll
     for (int c = 0; c < Sh::NC; ++c) asm volatile("" : "+v"(qop[c]));
+    int cow_src = -1, cow_dst = -1;
+    if constexpr (COW) {
+        pin_cow_pair(pair);
+        cow_pair_ids(a, pair, lane, cow_src, cow_dst);
+    }
     if (T <= 0 || T > a.max_seq_len) return;
     if ((T + BS - 1) / BS > a.max_blocks_per_seq) return;
     const int n_parts = (T + P - 1) / P;
@@ -209,6 +228,7 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
             if (b == 0 || idx < nblk) {
                 int pb = idx < 64 ? __builtin_amdgcn_readlane(ids, idx) : bt[idx];
                 if ((unsigned)pb >= (unsigned)a.num_blocks) { invalid = 1; pb = 0; }
+                if constexpr (COW) pb = cow_source(cow_src, cow_dst, pb);
                 tile = ((size_t)pb * a.num_kv_heads + kvh) * TILE;
                 if (b == 0) first = tile;
             }
@@ -423,16 +443,26 @@ decode_partition_mfma8_kernel(const DecodeArgs a) {
     }
 }
 
-template <int D, int BS, int W, int S>
-int launch_partition_mfma8(const DecodeArgs& a, hipStream_t stream) {
+template <int D, int BS, int W, int S, bool COW>
+int launch_partition_mfma8_as(const DecodeArgs& a, hipStream_t stream) {
     using Sh = MfmaShape<D, BS, W, S>;
-    auto kernel = decode_partition_mfma8_kernel<D, BS, W, S>;
+    auto kernel = decode_partition_mfma8_kernel<D, BS, W, S, COW>;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, Sh::LDS);
     if (attr != hipSuccess) return PA_ERR_LAUNCH;
-    const dim3 grid((unsigned)((size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
+    const size_t copies = COW ? 2 * (size_t)a.cow_num * cow_chunks<Fmt::FP8, D, BS, W * 64>(a.num_kv_heads) : 0;
+    const dim3 grid((unsigned)(copies + (size_t)a.num_seqs * a.max_partitions * a.num_kv_heads));
     hipLaunchKernelGGL(kernel, grid, dim3(W * 64), Sh::LDS, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// The copy-on-write instantiation when the launch carries pairs (never with
+// new tokens: this kernel does not store them).
+template <int D, int BS, int W, int S>
+int launch_partition_mfma8(const DecodeArgs& a, hipStream_t stream) {
+    if (a.new_k != nullptr) return PA_ERR_UNSUPPORTED;
+    return a.cow_num > 0 ? launch_partition_mfma8_as<D, BS, W, S, true>(a, stream)
+                         : launch_partition_mfma8_as<D, BS, W, S, false>(a, stream);
 }
 
 #ifndef PA_MFMA_WAVES

@@ -272,6 +272,9 @@ def test_decode_append_cow_validation(lib):
     assert _cow(lib, key=None) == NULL
     assert _cow(lib, value=None) == NULL
     assert _cow(lib, key=FAKE + 8) == SHAPE  # misaligned
+    # more pairs than one launch takes: the two-call path checks the rows before copying
+    assert _cow(lib, num_pairs=40, key=None) == NULL
+    assert _cow(lib, num_pairs=40, value=None) == NULL
 
 
 def _sp(lib, gs=FAKE, gp=FAKE, groups=4, mgs=16, mpl=1024, **kw):

@@ -9,7 +9,9 @@ token at the same row.  The fork's output is also checked against the oracle
 (copy, then store, then decode, from pools it builds itself).  The GQA-4
 kernel and the generic kernel (every other group and format) take the copies
 in their launch; the FP8 matrix-core shape (G = 8, head_dim 128) and more
-than 16 pairs make the two calls and must agree as well.
+than 16 pairs make the two calls and must agree as well.  Given no tokens,
+the call is pa_copy_blocks then pa_decode: one launch for the FP8
+matrix-core shape, two calls elsewhere, bitwise equal either way.
 
 The copy-on-write steps follow the explainer's section "Copy-on-Write（CoW）に
 よるメモリ共有" (copy the shared block, remap the writer's table entry)."""
@@ -23,7 +25,7 @@ import torch
 import oracle
 import paged_kv_cache_142_amd as pa
 import workloads
-from gpu_util import TOL, DeviceCase, assert_close, out_as_f64, poison_host, to_host_raw
+from gpu_util import TOL, DeviceCase, assert_close, oracle_out, oracle_pools, out_as_f64, poison_host, to_host_raw
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +191,61 @@ def test_cow_without_pairs_is_decode_with_append():
         kv_dtype="bf16", q_dtype="bf16", spare_blocks=4, num_copy_pairs=0, partition_size=512)
     print(f"[case] cow none {wl.name}", flush=True)
     _run(wl, np.zeros((0, 2), np.int64))
+
+
+
+def _run_no_tokens(wl):
+    """(output, K pool, V pool) bytes of pa_decode_append_cow without tokens
+    against pa_copy_blocks then pa_decode, after the step's scatter (quantized
+    on write for FP8 pools), with the workload's pairs."""
+    res = []
+    for fused in (True, False):
+        case = DeviceCase(wl)
+        if case.quantize_step:
+            pa.pa_reshape_and_cache_fp8(case.step_keys, case.step_values, case.k_cache, case.v_cache, case.k_scale,
+                                        case.v_scale, case.step_slots)
+        else:
+            pa.pa_reshape_and_cache(case.step_keys, case.step_values, case.k_cache, case.v_cache, case.step_slots)
+        if fused:
+            pa.pa_decode_append_cow(**case.decode_args(), key=None, value=None, block_pairs=case.pairs)
+        else:
+            pa.pa_copy_blocks(case.k_cache, case.v_cache, case.pairs)
+            case.decode()
+        torch.cuda.synchronize()
+        res.append((_bytes(case.out), _bytes(case.k_cache), _bytes(case.v_cache), case))
+    (o1, k1, v1, case), (o0, k0, v0, _) = res
+    assert np.array_equal(k0, k1), "K pool differs from copy + decode"
+    assert np.array_equal(v0, v1), "V pool differs from copy + decode"
+    assert np.array_equal(o0, o1), "output differs from copy + decode"
+    return case
+
+
+@pytest.mark.parametrize("kv,q,heads,kv_heads,block,P,npairs", [
+    ("fp8_e4m3", "bf16", 64, 8, 16, 512, 15),   # FP8 matrix-core shape: one launch
+    ("fp8_e4m3", "bf16", 64, 8, 32, 512, 15),
+    ("fp8_e4m3", "bf16", 64, 8, 16, 1024, 15),  # partitions of 64 blocks
+    ("fp8_e4m3", "bf16", 64, 8, 16, 512, 40),   # more pairs: the two calls
+    ("bf16", "bf16", 32, 8, 16, 512, 15),       # other shapes: the two calls
+])
+def test_cow_without_tokens_matches_copy_then_decode(kv, q, heads, kv_heads, block, P, npairs):
+    """Sources anywhere (no token is stored in the call, so a copy races with
+    nothing), destinations both spare blocks and blocks that tables name (read
+    through their sources), one pair outside the pool.  One case is also
+    checked against the oracle (scatter, copy, decode on its own pools)."""
+    wl = workloads.build_decode_workload(
+        f"cow_nt_{kv}_{heads}_{kv_heads}_{block}_{P}", 13, seq_lens=np.random.default_rng(13).integers(1, 3000, size=12),
+        num_heads=heads, num_kv_heads=kv_heads, head_dim=128, block_size=block, kv_dtype=kv, q_dtype=q,
+        spare_blocks=48, num_copy_pairs=npairs, partition_size=P)
+    pairs = wl.copy_pairs.copy()
+    # the first three destinations: blocks some table names, none of them a source
+    srcs = set(pairs[:, 0].tolist())
+    named = np.unique(wl.block_tables[wl.block_tables >= 0])
+    pairs[:3, 1] = [int(b) for b in np.random.default_rng(14).permutation(named) if int(b) not in srcs][:3]
+    pairs = np.concatenate([pairs, [[wl.num_blocks + 2, int(pairs[-1, 1])]]]).astype(np.int64)
+    wl = dataclasses.replace(wl, copy_pairs=pairs)
+    print(f"[case] cow without tokens {wl.name}: {len(pairs)} pairs", flush=True)
+    case = _run_no_tokens(wl)
+    if npairs == 15 and kv == "fp8_e4m3" and block == 16 and P == 512:
+        in_pool = dataclasses.replace(wl, copy_pairs=pairs[:-1])  # the oracle copies in-pool pairs only
+        kc, vc = oracle_pools(in_pool)
+        assert_close(out_as_f64(case.out), oracle_out(in_pool, kc, vc), TOL[kv], "copy + decode vs oracle")

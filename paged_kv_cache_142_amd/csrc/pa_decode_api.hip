@@ -190,15 +190,22 @@ __global__ void __launch_bounds__(REDUCE_THREADS) decode_reduce_kernel(const Dec
 #pragma unroll
     for (int u = 1; u < U; ++u) mx = fmaxf(mx, mv[u]);
     for (int p = pg + RG * U; merge && p < n_parts; p += RG) mx = fmaxf(mx, pm[(size_t)p * ms]);
-    if (c4 == 0) red_m[rw][pg] = mx;
-    __syncthreads();
-    float M = red_m[rw][0];
+    float M = mx;
+    if constexpr (RG > 1) {  // with one group every thread of the row already holds the row's maximum
+        if (c4 == 0) red_m[rw][pg] = mx;
+        __syncthreads();
+        M = red_m[rw][0];
 #pragma unroll
-    for (int r = 1; r < RG; ++r) M = fmaxf(M, red_m[rw][r]);
+        for (int r = 1; r < RG; ++r) M = fmaxf(M, red_m[rw][r]);
+    }
     add_batch(pg, M);
     for (int p0 = pg + RG * U; merge && p0 < n_parts; p0 += RG * U) {
         load_batch(p0);
         add_batch(p0, M);
+    }
+    if constexpr (RG == 1) {  // the thread holds its columns' whole sums: no exchange
+        if (merge) store4(float4{A.x / L, A.y / L, A.z / L, A.w / L});
+        return;
     }
     red_a[rw][pg][c4] = A;
     if (c4 == 0) red_l[rw][pg] = L;
